@@ -1,0 +1,64 @@
+"""Exact softmax attention restricted to the listed key blocks.
+
+TEST INFRASTRUCTURE (see the package docstring).
+
+"aclnnRainFusionAttention", Formula: the output is
+``softmax(scale * Q K^T + mask) V`` where the sparse block size is
+blockShapeX x blockShapeY and selectIdx says which key blocks each query block
+sees. Here the blocks are 128 x 128 and no additive mask is used (the
+arrangement does not pad; "RainFusion Attention", Geometry handling), so for
+a query row r of block q and query head n the key rows are exactly the rows of
+the blocks listed in ``select_idx[b*n_blocks + q, n, :select_num[...]]``;
+a short block contributes only its real rows. A row whose list is empty gets
+an all-zero output (reading: this only happens at sparsity 1 with no dense
+blocks).
+
+Float64 throughout: logits, the row maximum, exponentials, the row sum and
+the weighted sum of V.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .geometry import Plan
+
+
+def attention_block(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """Dense softmax attention of query rows ``q [M, D]`` over key rows ``k, v [L, D]`` (float64)."""
+    q = np.asarray(q, dtype=np.float64)
+    if k.shape[0] == 0:
+        return np.zeros((q.shape[0], v.shape[1]), dtype=np.float64)
+    logits = scale * (q @ np.asarray(k, dtype=np.float64).T)
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    return (e @ np.asarray(v, dtype=np.float64)) / e.sum(axis=1, keepdims=True)
+
+
+def listed_rows(p: Plan, ids) -> np.ndarray:
+    """Permuted row indices covered by the listed block ids, in list order."""
+    parts = [np.arange(p.blocks[j][0], p.blocks[j][0] + p.blocks[j][1]) for j in ids]
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+
+
+def sparse_attention(qp, kp, vp, p: Plan, select_idx, select_num, scale: float,
+                     query_blocks=None) -> np.ndarray:
+    """Permuted-order attention output ``[B, N1, S, D]`` (float64).
+
+    ``qp``: ``[B, N1, S, D]``; ``kp``, ``vp``: ``[B, N2, S, D]`` (permuted rows,
+    any real dtype). ``query_blocks``: optional iterable of ``(b, q, n)`` to
+    evaluate only those (query block, head) pairs; other rows stay zero.
+    """
+    B, N1, S, D = qp.shape
+    G = N1 // kp.shape[1]
+    nB = p.n_blocks
+    out = np.zeros((B, N1, S, D), dtype=np.float64)
+    todo = query_blocks if query_blocks is not None else (
+        (b, q, n) for b in range(B) for q in range(nB) for n in range(N1))
+    for b, q, n in todo:
+        r0, m = p.blocks[q]
+        row = b * nB + q
+        ids = select_idx[row, n, :select_num[row, n]]
+        rows = listed_rows(p, ids)
+        out[b, n, r0:r0 + m] = attention_block(qp[b, n, r0:r0 + m], kp[b, n // G, rows],
+                                               vp[b, n // G, rows], scale)
+    return out

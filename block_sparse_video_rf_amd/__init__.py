@@ -1,0 +1,12 @@
+"""RainFusion v2 block-sparse video attention for AMD MI355X (gfx950).
+
+The compute lives in the HIP library ``librf.so`` (C ABI in ``include/rf.h``);
+``rf`` is its ctypes binding. PyTorch supplies device memory and streams only.
+"""
+from .rf import (Buffers, Desc, RfError, RfPlanInfo, attention, load_library, rf_permute,
+                 rf_plan, rf_pool_select, rf_sparse_attn, rf_status_str, rf_unpermute,
+                 rf_version, EXPORTS, LIB_PATH)
+
+__all__ = ["Buffers", "Desc", "RfError", "RfPlanInfo", "attention", "load_library",
+           "rf_permute", "rf_plan", "rf_pool_select", "rf_sparse_attn", "rf_status_str",
+           "rf_unpermute", "rf_version", "EXPORTS", "LIB_PATH"]

@@ -1,0 +1,307 @@
+// Arrangement kernels: permute (+ block-mean pooling, + fp8 E4M3 quantisation
+// for the mix precision) and the inverse permutation.
+//
+// "RainFusion Attention" (introduction, Geometry handling) and the xLLM
+// pull request "feat: add RainFusion sparse attention for wan2.2" (commit
+// summary: frame-pairing rearrange of Q, K and V in one call; inverse
+// rearrange; roundtrip check). Block means as representative tokens: the
+// RainFusion2.0 abstract, insight 1.
+//
+// One launch covers Q, K and V: workgroup (block j, slot y) where y runs over
+// the B*N1 query heads, then the B*N2 key heads, then the B*N2 value heads.
+// A workgroup moves one block (<= 128 rows of D bf16) and never needs a map
+// in memory: rf_natural_row() decodes the source row from the geometry. The
+// work is a pure HBM stream (read once, write once); every 16-byte chunk is
+// one global load and one global store, rows of D*2 bytes are read whole.
+//
+// V is written block-transposed (vpt[b, n, j, d, c]) so that the attention
+// kernel's PV product reads its MFMA operand with contiguous 16-byte LDS
+// loads; the transpose goes through LDS here, where the work is bandwidth
+// bound anyway.
+#include <hip/hip_runtime.h>
+
+#include "rf_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+struct PermuteArgs {
+  RfGeom g;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* qp;
+  uint16_t* kp;
+  uint16_t* vpt;
+  float* q_pool;
+  float* k_pool;
+  uint8_t* q8;
+  uint8_t* k8;
+  float* q_scale;
+  float* k_scale;
+};
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// OCP E4M3, round to nearest even, finite inputs, saturating at +-448.
+__device__ __forceinline__ uint32_t e4m3_rne(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  const float af = __uint_as_float(a);
+  if (af >= 448.0f) return sign | 0x7eu;
+  if (af < 0.015625f) {                        // below 2^-6: fixed quantum 2^-9
+    const float m = __builtin_rintf(af * 512.0f);  // exact scaling, ties to even
+    return sign | (uint32_t)m;                 // m == 8 encodes 2^-6 (exponent field 1)
+  }
+  const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);  // keep 3 mantissa bits, ties to even
+  const uint32_t e = (r >> 23) - 127u + 7u;
+  return sign | (e << 3) | ((r >> 20) & 7u);
+}
+
+// Block-wide reductions over 256 threads through LDS, fixed order.
+__device__ __forceinline__ float block_max(float x, float* red) {
+  const int tid = threadIdx.x;
+  red[tid] = x;
+  __syncthreads();
+  for (int off = kThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
+  constexpr int C = D / 8;                 // 16-byte chunks per row
+  constexpr int RPP = kThreads / C;        // rows per pass
+  constexpr int PASSES = 128 / RPP;
+  const RfGeom& g = a.g;
+  const int tid = threadIdx.x;
+  const int c = tid % C;
+  const int rsub = tid / C;
+  const int32_t j = blockIdx.x;
+  int32_t y = blockIdx.y;
+
+  // Which tensor, batch item and head.
+  int kind;  // 0 = Q, 1 = K, 2 = V
+  int heads;
+  if (y < g.B * g.N1) {
+    kind = 0;
+    heads = g.N1;
+  } else if (y < g.B * (g.N1 + g.N2)) {
+    kind = 1;
+    y -= g.B * g.N1;
+    heads = g.N2;
+  } else {
+    kind = 2;
+    y -= g.B * (g.N1 + g.N2);
+    heads = g.N2;
+  }
+  const int32_t b = y / heads, n = y % heads;
+  const uint16_t* src = kind == 0 ? a.q : (kind == 1 ? a.k : a.v);
+  if (src == nullptr) return;  // uniform over the workgroup
+
+  int64_t row0;
+  int32_t len;
+  rf_block_rows(g, j, &row0, &len);
+
+  uint4 val[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int i = p * RPP + rsub;
+    if (i < len) {
+      const int64_t nat = rf_natural_row(g, row0 + i);
+      val[p] = *reinterpret_cast<const uint4*>(src + rf_row_offset(g, g.layout, heads, b, n, nat) +
+                                               c * 8);
+    } else {
+      val[p] = make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  __shared__ float red[kThreads * 8 > 128 * (D + 8) / 2 ? kThreads * 8 : 128 * (D + 8) / 2];
+
+  if (kind == 2) {
+    // V: stage the block in LDS, then write it transposed [D][128] with zero
+    // columns past the block's length.
+    uint16_t* tile = reinterpret_cast<uint16_t*>(red);  // [128][D + 8]
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int i = p * RPP + rsub;
+      *reinterpret_cast<uint4*>(tile + i * (D + 8) + c * 8) = val[p];
+    }
+    __syncthreads();
+    uint16_t* dst = a.vpt + (((int64_t)b * g.N2 + n) * g.n_blocks + j) * (int64_t)D * 128;
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m) {
+      const int qd = tid + kThreads * m;
+      const int d = qd / 16, cc = qd % 16;
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = tile[(cc * 8 + 2 * e) * (D + 8) + d];
+        const uint32_t hi = tile[(cc * 8 + 2 * e + 1) * (D + 8) + d];
+        w[e] = lo | (hi << 16);
+      }
+      *reinterpret_cast<uint4*>(dst + d * 128 + cc * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    return;
+  }
+
+  // Q or K: permuted bf16 copy.
+  uint16_t* dstp = kind == 0 ? a.qp : a.kp;
+  if (dstp) {
+    const int64_t base = (((int64_t)b * heads + n) * g.S + row0) * D;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int i = p * RPP + rsub;
+      if (i < len) *reinterpret_cast<uint4*>(dstp + base + (int64_t)i * D + c * 8) = val[p];
+    }
+  }
+
+  // Block mean of a sparse block (fp32, fixed summation order).
+  float* pool = kind == 0 ? a.q_pool : a.k_pool;
+  const bool sparse_blk = j >= g.n_head && j < g.n_head + g.n_sparse;
+  if (pool && sparse_blk) {
+    float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const uint32_t w[4] = {val[p].x, val[p].y, val[p].z, val[p].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[2 * e] += bf_lo(w[e]);
+        s[2 * e + 1] += bf_hi(w[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[rsub * D + c * 8 + e] = s[e];
+    __syncthreads();
+    if (tid < D) {
+      float t = 0.0f;
+      for (int r = 0; r < RPP; ++r) t += red[r * D + tid];
+      const int32_t js = j - g.n_head;
+      pool[(((int64_t)b * heads + n) * g.n_sparse + js) * D + tid] = t * (1.0f / 128.0f);
+    }
+    __syncthreads();
+  }
+
+  // Mix precision: per-block E4M3 codes and scale.
+  uint8_t* q8 = kind == 0 ? a.q8 : a.k8;
+  if (q8) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const uint32_t w[4] = {val[p].x, val[p].y, val[p].z, val[p].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        amax = fmaxf(amax, fmaxf(fabsf(bf_lo(w[e])), fabsf(bf_hi(w[e]))));
+    }
+    amax = block_max(amax, red);
+    const float r = amax > 0.0f ? 448.0f / amax : 1.0f;
+    const float sigma = amax > 0.0f ? amax / 448.0f : 1.0f;
+    const int64_t base = (((int64_t)b * heads + n) * g.S + row0) * D;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int i = p * RPP + rsub;
+      if (i < len) {
+        const uint32_t w[4] = {val[p].x, val[p].y, val[p].z, val[p].w};
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          lo |= e4m3_rne(bf_lo(w[e]) * r) << (16 * e);
+          lo |= e4m3_rne(bf_hi(w[e]) * r) << (16 * e + 8);
+          hi |= e4m3_rne(bf_lo(w[e + 2]) * r) << (16 * e);
+          hi |= e4m3_rne(bf_hi(w[e + 2]) * r) << (16 * e + 8);
+        }
+        *reinterpret_cast<uint2*>(q8 + base + (int64_t)i * D + c * 8) = make_uint2(lo, hi);
+      }
+    }
+    float* sc = kind == 0 ? a.q_scale : a.k_scale;
+    if (tid == 0) sc[((int64_t)b * heads + n) * g.n_blocks + j] = sigma;
+  }
+}
+
+struct UnpermuteArgs {
+  RfGeom g;
+  const uint16_t* out_p;
+  uint16_t* out;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void unpermute_kernel(UnpermuteArgs a) {
+  constexpr int C = D / 8;
+  constexpr int RPP = kThreads / C;
+  constexpr int PASSES = 128 / RPP;
+  const RfGeom& g = a.g;
+  const int tid = threadIdx.x;
+  const int c = tid % C, rsub = tid / C;
+  const int32_t j = blockIdx.x;
+  const int32_t b = blockIdx.y / g.N1, n = blockIdx.y % g.N1;
+  int64_t row0;
+  int32_t len;
+  rf_block_rows(g, j, &row0, &len);
+  const uint16_t* src = a.out_p + (((int64_t)b * g.N1 + n) * g.S + row0) * D;
+  uint4 val[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int i = p * RPP + rsub;
+    if (i < len) val[p] = *reinterpret_cast<const uint4*>(src + (int64_t)i * D + c * 8);
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int i = p * RPP + rsub;
+    if (i < len) {
+      const int64_t nat = rf_natural_row(g, row0 + i);
+      *reinterpret_cast<uint4*>(a.out + rf_row_offset(g, g.layout, g.N1, b, n, nat) + c * 8) =
+          val[p];
+    }
+  }
+}
+
+}  // namespace
+
+rf_status rf_launch_permute(const RfGeom& g, int32_t precision, const void* q, const void* k,
+                            const void* v, void* qp, void* kp, void* vpt, float* q_pool,
+                            float* k_pool, uint8_t* q8, uint8_t* k8, float* q_scale,
+                            float* k_scale, void* stream) {
+  (void)precision;
+  PermuteArgs a;
+  a.g = g;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.qp = static_cast<uint16_t*>(qp);
+  a.kp = static_cast<uint16_t*>(kp);
+  a.vpt = static_cast<uint16_t*>(vpt);
+  a.q_pool = q_pool;
+  a.k_pool = k_pool;
+  a.q8 = q8;
+  a.k8 = k8;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  const dim3 grid(g.n_blocks, g.B * (g.N1 + 2 * g.N2));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g.D == 128)
+    hipLaunchKernelGGL(permute_kernel<128>, grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(permute_kernel<64>, grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError() == hipSuccess ? RF_OK : RF_ERR_HIP;
+}
+
+rf_status rf_launch_unpermute(const RfGeom& g, const void* out_p, void* out, void* stream) {
+  UnpermuteArgs a;
+  a.g = g;
+  a.out_p = static_cast<const uint16_t*>(out_p);
+  a.out = static_cast<uint16_t*>(out);
+  const dim3 grid(g.n_blocks, g.B * g.N1);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g.D == 128)
+    hipLaunchKernelGGL(unpermute_kernel<128>, grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(unpermute_kernel<64>, grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError() == hipSuccess ? RF_OK : RF_ERR_HIP;
+}

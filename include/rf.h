@@ -1,0 +1,213 @@
+/*
+ * rf.h - C ABI of the RainFusion v2 block-sparse video attention path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The path has five steps, each an entry point below except the host-only
+ * plan:
+ *   rf_plan         host: validate a call, derive the arrangement and sizes
+ *   rf_permute      arrange Q/K/V into 128-token space-time blocks, pool the
+ *                   sparse blocks, and (mix precision) quantise Q/K to fp8
+ *   rf_pool_select  score pooled blocks and build selectIdx / selectNum
+ *   rf_sparse_attn  exact softmax attention restricted to the listed blocks
+ *   rf_unpermute    undo the arrangement
+ *
+ * Sources (cited by page title and section):
+ *   [RFA]  "RainFusion Attention" (vLLM-Omni user guide for the
+ *          RAINFUSION_ATTN backend): introduction, Configuration, Geometry
+ *          handling.
+ *   [XPR]  "feat: add RainFusion sparse attention for wan2.2" (xLLM pull
+ *          request): commit summary (frame-pairing rearrange, roundtrip).
+ *   [ACL]  "aclnnRainFusionAttention" (CANN operator reference): Formula,
+ *          the two-phase workspace/execute pattern, the constraint list.
+ *   [RF2]  "RainFusion2.0: Temporal-Spatial Awareness and Hardware-Efficient
+ *          Block-wise Sparse Attention": abstract (block-mean representative
+ *          tokens, spatiotemporal permutation, first-frame sink).
+ *
+ * Conventions for every entry point:
+ *   - The caller owns all memory. Device pointers point to HIP device memory
+ *     of the current device; the library never allocates, frees or
+ *     synchronises, and keeps no mutable global state (calls are thread-safe).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is only enqueued on it.
+ *   - Every argument is validated on the host before anything is enqueued;
+ *     on any error nothing is enqueued and the status says why.
+ *   - Launch failures return RF_ERR_HIP.
+ *   - Results are deterministic: no floating-point atomics anywhere ([ACL]
+ *     constraints: deterministic by default).
+ *   - Outputs never alias inputs (out-of-place only).
+ *
+ * Element types: Q, K, V and the output are bf16 (raw 16-bit patterns);
+ * [ACL] also allows fp16, which this library rejects (RF_ERR_DTYPE).
+ */
+#ifndef RF_H_
+#define RF_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rf_status {
+  RF_OK = 0,
+  RF_ERR_NULL = 1,         /* a required pointer is NULL */
+  RF_ERR_LAYOUT = 2,       /* layout is neither BNSD nor TND ([ACL] constraints) */
+  RF_ERR_DTYPE = 3,        /* element type other than bf16 */
+  RF_ERR_SHAPE = 4,        /* batch/heads/head_dim/seq_len out of range */
+  RF_ERR_BLOCK_SHAPE = 5,  /* block shape not {128, 128} ([ACL]: entries > 0; only 128 built) */
+  RF_ERR_GQA = 6,          /* heads_q not a multiple of heads_kv ([ACL] constraints) */
+  RF_ERR_SPARSITY = 7,     /* sparsity not finite or outside [0, 1] ([RFA] Configuration) */
+  RF_ERR_GEOMETRY = 8,     /* grid / prefix / first frame inconsistent with seq_len */
+  RF_ERR_WORKSPACE = 9,    /* workspace smaller than rf_plan says */
+  RF_ERR_UNSUPPORTED = 10, /* valid per the pages but not built here (see the field docs) */
+  RF_ERR_PRECISION = 11,   /* unknown precision, or a buffer its precision needs is NULL */
+  RF_ERR_HIP = 12,         /* a HIP launch failed */
+  RF_ERR_ALIAS = 13        /* an output aliases an input */
+} rf_status;
+
+typedef enum rf_layout {
+  RF_LAYOUT_BNSD = 0, /* [B, N, S, D], rows of D contiguous */
+  RF_LAYOUT_TND = 1   /* [B*S, N, D]: token-major, batch items stacked */
+} rf_layout;
+
+typedef enum rf_dtype { RF_DTYPE_BF16 = 0, RF_DTYPE_FP16 = 1 /* rejected */ } rf_dtype;
+
+typedef enum rf_precision {
+  RF_PREC_BF16 = 0, /* bf16 Q/K/V, bf16 MFMA, fp32 softmax ([ACL]: fp32 softmax for bf16) */
+  RF_PREC_MIX = 1,  /* Q/K as fp8 E4M3 with one fp32 scale per (batch, head, 128-row
+                       block); V, probabilities and output bf16; fp32 softmax.
+                       [RFA] Configuration names "mix" without defining it. */
+  RF_PREC_FP8 = 2   /* all-fp8 mode named by [RFA]; not built: RF_ERR_UNSUPPORTED */
+} rf_precision;
+
+/* One attention call. Sizes are per batch item; all batch items share the
+ * same geometry. */
+typedef struct rf_desc {
+  int32_t layout;            /* rf_layout, for q/k/v and the final output */
+  int32_t dtype;             /* rf_dtype; only RF_DTYPE_BF16 */
+  int32_t batch;             /* B >= 1 */
+  int32_t heads_q;           /* N1 >= 1 */
+  int32_t heads_kv;          /* N2 >= 1, N1 % N2 == 0; query head n uses KV head n / (N1/N2) */
+  int32_t head_dim;          /* D: 64 or 128 */
+  int64_t seq_len;           /* S rows per batch item */
+  int32_t block_shape[2];    /* {blockShapeX, blockShapeY} ([ACL]); must be {128, 128} */
+  int64_t prefix_len;        /* rows before the video (text, conditions, audio): always dense ([RFA]) */
+  int64_t first_frame_rows;  /* 0, or grid_h*grid_w: first latent frame is the dense sink ([RF2]) */
+  int32_t grid_t, grid_h, grid_w; /* latent video grid; all 0 = no geometry -> dense */
+  int32_t precision;         /* rf_precision */
+  double sparsity;           /* nominal dropped fraction of sparse key blocks, finite, in [0, 1] ([RFA]) */
+  float scale;               /* softmax scale > 0 (usually 1/sqrt(D)) */
+  int32_t min_sparse_blocks; /* fewer sparse blocks than this -> dense; [RFA] uses 32; <= 0 means 32 */
+} rf_desc;
+
+/* What rf_plan derives (all host-side). Block ids run over the permuted
+ * sequence: head blocks [0, n_head), sparse blocks [n_head, n_head+n_sparse),
+ * tail blocks after. */
+typedef struct rf_plan_info {
+  int32_t dense_fallback;   /* 1: every query block attends to every block ([RFA] introduction) */
+  int32_t n_blocks;         /* n_head + n_sparse + n_tail */
+  int32_t n_head;           /* ceil((prefix_len + first_frame_rows) / 128) */
+  int32_t n_sparse;         /* frame pairs x (grid_h/8) x (grid_w/8) */
+  int32_t n_tail;           /* ceil(promoted_rows / 128) */
+  int32_t topk;             /* sparse key blocks kept per sparse query block:
+                               n_sparse - floor(sparsity*n_sparse + 1e-6) */
+  int32_t max_kv_blocks;    /* width of selectIdx: n_blocks */
+  int32_t select_rows;      /* rows of selectIdx / selectNum: batch * n_blocks */
+  int64_t head_rows;        /* prefix + first frame (seq_len on fallback) */
+  int64_t sparse_rows;      /* 128 * n_sparse */
+  int64_t promoted_rows;    /* video rows moved to the dense tail ([RFA] Geometry handling) */
+  int64_t qp_elems;         /* bf16 elements of qp / out_p: batch*heads_q*seq_len*head_dim */
+  int64_t kp_elems;         /* bf16 elements of kp: batch*heads_kv*seq_len*head_dim */
+  int64_t vpt_elems;        /* bf16 elements of vpt: batch*heads_kv*n_blocks*head_dim*128 */
+  int64_t q_pool_elems;     /* fp32 elements of q_pool: batch*heads_q*n_sparse*head_dim */
+  int64_t k_pool_elems;     /* fp32 elements of k_pool: batch*heads_kv*n_sparse*head_dim */
+  int64_t q_scale_elems;    /* fp32 elements of q_scale (mix): batch*heads_q*n_blocks */
+  int64_t k_scale_elems;    /* fp32 elements of k_scale (mix): batch*heads_kv*n_blocks */
+  size_t ws_select_bytes;   /* workspace of rf_pool_select */
+} rf_plan_info;
+
+/* Validate `desc` and derive the arrangement. Host only: touches no device,
+ * so it can run on a machine without a GPU. */
+rf_status rf_plan(const rf_desc* desc, rf_plan_info* info);
+
+/* Step 1 (+ pooling, + mix quantisation). [RFA] introduction and Geometry
+ * handling; [XPR] commit summary (frame pairs, one call for Q, K and V);
+ * [RF2] abstract (spatiotemporal permutation, block means).
+ *
+ * Permuted order of each batch item: prefix rows; the first frame (if any);
+ * the sparse blocks, each one 2 frames x 8x8 tile box numbered (pair, tile
+ * row, tile column), tokens (dt, dh, dw) in raster order; then the promoted
+ * rows (those that fit no box) in natural order. Video token (t, h, w) sits
+ * at natural row prefix_len + (t*grid_h + h)*grid_w + w.
+ *
+ * Inputs (device, caller layout): q [.., heads_q, ..], k and v [.., heads_kv, ..].
+ * Any of q, k, v may be NULL to skip that tensor.
+ * Outputs (device), all optional unless stated:
+ *   qp     bf16 [B, N1, S, D] permuted rows (BNSD whatever the input layout)
+ *   kp     bf16 [B, N2, S, D]
+ *   vpt    bf16 [B, N2, n_blocks, D, 128]: V block-transposed, vpt[b,n,j,d,c]
+ *          = V row c of block j, channel d; columns c >= the block's length are 0.
+ *          Required when v is given (it is the layout rf_sparse_attn reads).
+ *   q_pool fp32 [B, N1, n_sparse, D] mean of each sparse block of Q
+ *   k_pool fp32 [B, N2, n_sparse, D] mean of each sparse block of K
+ *   q8,k8  uint8 E4M3 codes, same shape as qp/kp   (mix; required in mix mode)
+ *   q_scale,k_scale fp32 [B, N, n_blocks] per-block scales (mix; required)
+ * Mix quantisation of a block: amax = max |x|; r = 448.0f / amax;
+ * code = E4M3 round-to-nearest-even, saturating at 448, of (float)(x * r);
+ * scale = amax / 448.0f; an all-zero block gets r = scale = 1. */
+rf_status rf_permute(const rf_desc* desc, const void* q, const void* k, const void* v,
+                     void* qp, void* kp, void* vpt, float* q_pool, float* k_pool,
+                     uint8_t* q8, uint8_t* k8, float* q_scale, float* k_scale, void* stream);
+
+/* Steps 2-3. [RFA] introduction (pool 128-token blocks, rank per query
+ * block, keep the highest-scoring); [RF2] abstract (block means as
+ * representative tokens); [ACL] constraints (selectIdx [T, heads, maxKv]
+ * with T = batch * query blocks, -1 fill; selectNum [T, heads]).
+ *
+ * q_pool / k_pool: pooled blocks as written by rf_permute. If either is NULL
+ * it is recomputed from qp / kp into the workspace.
+ * Score of query block i against key block j, query head n:
+ *   scale * <q_pool[n, i], k_pool[n / G, j]>  (fp32).
+ * A sparse query block keeps the topk highest-scoring sparse key blocks
+ * (equal scores: lower id first) plus every head and tail block; its list is
+ * sorted ascending. Head and tail query blocks list every block. Unused list
+ * entries are -1.
+ * Outputs: select_idx int32 [select_rows, N1, max_kv] (max_kv >= n_blocks),
+ *          select_num int32 [select_rows, N1].
+ * Workspace: device, at least ws_select_bytes (from rf_plan). */
+rf_status rf_pool_select(const rf_desc* desc, const void* qp, const void* kp,
+                         const float* q_pool, const float* k_pool, int32_t* select_idx,
+                         int32_t* select_num, int32_t max_kv, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Step 4. [ACL] Formula: out = softmax(scale * Q K^T) V over the key rows of
+ * the listed 128x128 blocks (no additive mask; short blocks contribute only
+ * their real rows). fp32 accumulation and fp32 online softmax.
+ * bf16 precision reads qp, kp, vpt; mix precision reads q8, k8, q_scale,
+ * k_scale, vpt (logits = scale * q_scale * k_scale * <q8, k8>).
+ * select_idx / select_num as above (any list the caller builds is accepted:
+ * entries outside [0, n_blocks) are skipped, counts are clamped to max_kv).
+ * A row with an empty list gets zeros.
+ * out_p: bf16 [B, N1, S, D], permuted row order, rounded to nearest even. */
+rf_status rf_sparse_attn(const rf_desc* desc, const void* qp, const void* kp, const void* vpt,
+                         const uint8_t* q8, const uint8_t* k8, const float* q_scale,
+                         const float* k_scale, const int32_t* select_idx,
+                         const int32_t* select_num, int32_t max_kv, void* out_p, void* stream);
+
+/* Step 5. [XPR] commit summary (inverse rearrange; roundtrip check).
+ * out[natural row pi(r)] = out_p[r]; out in the caller's layout with heads_q
+ * heads. */
+rf_status rf_unpermute(const rf_desc* desc, const void* out_p, void* out, void* stream);
+
+/* Short English text for a status code (static storage). */
+const char* rf_status_str(rf_status status);
+
+/* Library version string (static storage). */
+const char* rf_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RF_H_ */

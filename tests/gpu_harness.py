@@ -1,0 +1,116 @@
+"""Helpers shared by the GPU parity tests: move seeded inputs to the device,
+run the HIP path through the C ABI binding, run the oracle on the same bytes,
+and compare with the stated rules.
+
+Comparison rules:
+* permuted copies, E4M3 codes, block scales, selectNum and the dense part of
+  every selectIdx row: bit-exact;
+* the chosen sparse blocks of a row: identical sets, except that a block may
+  be swapped for another when both oracle scores are within
+  1e-5 * max|score| of the oracle's k-th score (the order of near-equal fp32
+  sums is not fixed);
+* pooled means: |gpu - oracle| <= 2e-6 (fp32 sums of 128 bf16 values);
+* attention output: max-abs <= 2e-2 and mean-abs <= 2e-3 against the float64
+  oracle (bf16), 6e-2 / 6e-3 for the mix precision.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+
+import oracle
+from oracle.geometry import Geometry
+from synth import bf16_to_f32
+
+BF16_TOL = (2e-2, 2e-3)
+MIX_TOL = (6e-2, 6e-3)
+NEAR_TIE_REL = 1e-5
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(u16):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16)
+    return t.cuda()
+
+
+def to_host_u16(t):
+    import torch
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def geometry_of(desc) -> Geometry:
+    grid = tuple(desc.grid)
+    return Geometry(desc.prefix_len if any(grid) else desc.seq_len,
+                    grid if any(grid) else None, bool(desc.first_frame_rows), desc.sparsity,
+                    min_sparse_blocks=desc.min_sparse_blocks)
+
+
+def run_gpu(desc, q, k, v):
+    """Run the four entry points on device copies of the bf16 bit arrays ``q, k, v``."""
+    import torch
+    import block_sparse_video_rf_amd as rf
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    out, bufs = rf.attention(qd, kd, vd, desc)
+    torch.cuda.synchronize()
+    return dict(out=out, bufs=bufs, q=qd, k=kd, v=vd)
+
+
+def expected_vpt(vp_u16, p, D):
+    """Block-transposed V ``[B, N, nB, D, 128]`` (zero past a short block)."""
+    B, N = vp_u16.shape[:2]
+    out = np.zeros((B, N, p.n_blocks, D, 128), dtype=np.uint16)
+    for j, (r0, n) in enumerate(p.blocks):
+        out[:, :, j, :, :n] = vp_u16[:, :, r0:r0 + n, :].transpose(0, 1, 3, 2)
+    return out
+
+
+def check_selection(p, batch, heads_q, gpu_idx, gpu_num, scores, max_kv=None):
+    """Compare GPU selectIdx/selectNum with the oracle's rule (near-ties allowed)."""
+    nB = p.n_blocks
+    max_kv = nB if max_kv is None else max_kv
+    o_idx, o_num = oracle.select_lists(p, batch, heads_q, scores)
+    assert np.array_equal(gpu_num, o_num), "selectNum differs"
+    assert gpu_idx.shape == (batch * nB, heads_q, max_kv)
+    swaps = 0
+    for row in range(batch * nB):
+        b, q = divmod(row, nB)
+        for n in range(heads_q):
+            m = o_num[row, n]
+            g_row, o_row = gpu_idx[row, n], o_idx[row, n]
+            assert np.all(g_row[m:] == -1), (row, n)
+            if np.array_equal(g_row[:m], o_row[:m]):
+                continue
+            assert p.is_sparse_block(q), (row, n, "dense row differs")
+            g_set, o_set = set(g_row[:m].tolist()), set(o_row[:m].tolist())
+            assert np.all(np.diff(g_row[:m]) > 0), (row, n, "not ascending")
+            dense = set(range(p.n_head)) | set(range(p.n_head + p.n_sparse, nB))
+            assert dense <= g_set, (row, n, "dense block missing")
+            sc = scores[b, n, q - p.n_head]
+            kth = np.sort(sc)[::-1][p.topk - 1]
+            tol = NEAR_TIE_REL * np.abs(sc).max()
+            for j in g_set ^ o_set:
+                assert abs(sc[j - p.n_head] - kth) <= tol, (row, n, j, sc[j - p.n_head], kth)
+            swaps += 1
+    return swaps
+
+
+def attention_error(gpu_out_f32, ref):
+    err = np.abs(gpu_out_f32.astype(np.float64) - ref)
+    return float(err.max()), float(err.mean())
+
+
+def assert_close(gpu_out_f32, ref, tol, what=""):
+    mx, mean = attention_error(gpu_out_f32, ref)
+    log(f"  {what} max-abs {mx:.3e} mean-abs {mean:.3e} (tol {tol[0]:.0e}/{tol[1]:.0e})")
+    assert mx <= tol[0] and mean <= tol[1], (what, mx, mean)
+
+
+def f32(u16):
+    return bf16_to_f32(u16)

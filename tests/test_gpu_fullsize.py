@@ -1,0 +1,104 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (the same four entry points, BNSD, one call each).
+
+Everything the oracle can do quickly is compared in full: permuted Q/K and
+block-transposed V (bit-exact), pooled means, E4M3 codes and scales (mix,
+bit-exact), selectIdx / selectNum over every row (bit-exact up to near-ties).
+The attention output is compared on sampled (query block, head) pairs that
+the float64 oracle computes one by one - every kind of query block (head,
+sparse, tail) is sampled - through the inverse arrangement.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle.geometry import plan, permutation
+from synth import WORKLOADS, make_qkv
+
+from gpu_harness import (BF16_TOL, MIX_TOL, assert_close, check_selection, expected_vpt, f32,
+                         geometry_of, log, run_gpu, to_host_u16)
+
+pytestmark = pytest.mark.gpu
+
+
+def _samples(p, heads, rng, n_sparse=24):
+    picks = []
+    dense = list(range(p.n_head)) + list(range(p.n_head + p.n_sparse, p.n_blocks))
+    for q in (dense[0], dense[-1]):
+        picks.append((0, q, int(rng.integers(heads))))
+    for _ in range(n_sparse):
+        picks.append((0, int(rng.integers(p.n_head, p.n_head + p.n_sparse)),
+                      int(rng.integers(heads))))
+    return sorted(set(picks))
+
+
+@pytest.mark.parametrize("name", ["wan22", "minimax_h3", "wan22_mix", "gqa_long"])
+def test_full_size(name):
+    import block_sparse_video_rf_amd as rf
+    w = WORKLOADS[name]
+    desc = rf.Desc.from_workload(w)
+    log(f"[full {name}] N={w.heads_q}/{w.heads_kv} S={w.seq_len} grid={w.grid} s={w.sparsity} "
+        f"{w.precision}")
+    q, k, v = make_qkv(w)
+    log("  inputs ready")
+    res = run_gpu(desc, q, k, v)
+    bufs = res["bufs"]
+    log("  gpu done")
+    g = geometry_of(desc)
+    p = plan(g)
+    pi = permutation(g)
+    qp_o, kp_o, vp_o = (oracle.permute_rows(x, pi) for x in (q, k, v))
+    if bufs.qp is not None:
+        assert np.array_equal(to_host_u16(bufs.qp), qp_o)
+        assert np.array_equal(to_host_u16(bufs.kp), kp_o)
+    assert np.array_equal(to_host_u16(bufs.vpt), expected_vpt(vp_o, p, w.head_dim))
+    log("  permute bit-exact")
+    qpool_o = oracle.pool_blocks(f32(qp_o), p)
+    kpool_o = oracle.pool_blocks(f32(kp_o), p)
+    assert np.abs(bufs.q_pool.cpu().numpy() - qpool_o).max() <= 2e-6
+    assert np.abs(bufs.k_pool.cpu().numpy() - kpool_o).max() <= 2e-6
+    log("  pools within 2e-6")
+    scale = 1.0 / np.sqrt(w.head_dim)
+    scores = oracle.block_scores(qpool_o, kpool_o, scale)
+    gi = bufs.select_idx.cpu().numpy()
+    gn = bufs.select_num.cpu().numpy()
+    swaps = check_selection(p, w.batch, w.heads_q, gi, gn, scores)
+    log(f"  selection exact ({swaps} near-tie rows)")
+    q_att, k_att = f32(qp_o), f32(kp_o)
+    if w.precision == "mix":
+        q8, sq = oracle.quantize_blocks(q_att, p)
+        k8, sk = oracle.quantize_blocks(k_att, p)
+        assert np.array_equal(bufs.q8.cpu().numpy(), q8)
+        assert np.array_equal(bufs.k8.cpu().numpy(), k8)
+        assert np.array_equal(bufs.q_scale.cpu().numpy(), sq)
+        assert np.array_equal(bufs.k_scale.cpu().numpy(), sk)
+        log("  fp8 codes and scales bit-exact")
+    rng = np.random.default_rng(11)
+    picks = _samples(p, w.heads_q, rng)
+    out_nat = f32(to_host_u16(res["out"]))
+    vp_f = f32(vp_o)
+    G = w.heads_q // w.heads_kv
+    worst = [0.0, 0.0]
+    for b, qb, n in picks:
+        r0, m = p.blocks[qb]
+        ids = gi[qb, n, :gn[qb, n]]
+        rows = oracle.attention.listed_rows(p, ids)
+        refs = []
+        if w.precision == "mix":
+            qd = oracle.e4m3_decode(q8[b, n, r0:r0 + m]) * sq[b, n, qb]
+            kd = np.concatenate([oracle.e4m3_decode(k8[b, n // G, p.blocks[j][0]:
+                                                      p.blocks[j][0] + p.blocks[j][1]])
+                                 * sk[b, n // G, j] for j in ids])
+            refs.append((oracle.attention_block(qd, kd, vp_f[b, n // G, rows], scale), BF16_TOL))
+            refs.append((oracle.attention_block(q_att[b, n, r0:r0 + m], k_att[b, n // G, rows],
+                                                vp_f[b, n // G, rows], scale), MIX_TOL))
+        else:
+            refs.append((oracle.attention_block(q_att[b, n, r0:r0 + m], k_att[b, n // G, rows],
+                                                vp_f[b, n // G, rows], scale), BF16_TOL))
+        got = out_nat[b, n, pi[r0:r0 + m]]  # through the inverse arrangement
+        for ref, tol in refs:
+            err = np.abs(got.astype(np.float64) - ref)
+            assert err.max() <= tol[0] and err.mean() <= tol[1], (b, qb, n, err.max(), err.mean())
+            worst = [max(worst[0], err.max()), max(worst[1], err.mean())]
+    log(f"  attention on {len(picks)} sampled blocks: worst max-abs {worst[0]:.3e} "
+        f"mean-abs {worst[1]:.3e}")

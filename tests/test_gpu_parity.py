@@ -1,0 +1,223 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small cases run every step in full: permuted copies (bit-exact), block
+transposed V (bit-exact), pooled means, selectIdx/selectNum (bit-exact up to
+documented near-ties), attention (oracle fed the GPU's own lists, and end to
+end), the unpermuted output, and E4M3 codes/scales in mix precision. They span
+several 128-row tiles and ragged tails: a prefix that is not a multiple of
+128, unaligned grid height and width, an unpaired last frame, a short last
+block, GQA, TND with batch 2, head_dim 64 and 128, and the degenerate cases
+(dense fallback below 32 blocks, sparsity 0, sparsity 1 with empty lists).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle.geometry import plan, permutation
+from synth import WORKLOADS, Workload, make_qkv, to_tnd, from_tnd
+
+from gpu_harness import (BF16_TOL, MIX_TOL, assert_close, check_selection, expected_vpt, f32,
+                         geometry_of, log, run_gpu, to_host_u16)
+
+pytestmark = pytest.mark.gpu
+
+
+def _custom(name, batch, hq, hkv, d, prefix, grid, f0, s, precision="bf16", smooth=True, seed=7):
+    return Workload(name, batch, hq, hkv, d, prefix, grid, f0, s, precision, smooth, seed)
+
+
+SMALL = {
+    "tiny": (WORKLOADS["tiny"], {}),
+    "tiny_mix": (WORKLOADS["tiny"].with_(precision="mix"), {}),
+    "tiny_tnd_b2": (WORKLOADS["tiny"].with_(batch=2), {"layout": "TND"}),
+    # prefix not a multiple of 128, unaligned h and w, unpaired last frame, GQA 4/2, D=128
+    "ragged_gqa": (_custom("ragged_gqa", 1, 4, 2, 128, 200, (10, 17, 34), True, 0.8), {}),
+    "ragged_gqa_mix": (_custom("ragged_gqa", 1, 4, 2, 128, 200, (10, 17, 34), True, 0.8,
+                               precision="mix"), {}),
+    # MiniMax-like unaligned width, no first frame: a 32-row last tail block
+    "minimax_small": (_custom("minimax_small", 1, 2, 2, 128, 512, (6, 24, 42), False, 0.8), {}),
+    "minimax_small_tnd": (_custom("minimax_small", 1, 2, 2, 128, 512, (6, 24, 42), False, 0.8),
+                          {"layout": "TND"}),
+    # sparsity 0.5, D=64, GQA 2/1, batch 2
+    "b2_gqa_d64": (_custom("b2_gqa_d64", 2, 2, 1, 64, 77, (5, 16, 40), True, 0.5), {}),
+    # dense fallback: 31 sparse blocks (below 32) and exactly 32
+    "fallback_31": (_custom("fallback_31", 1, 2, 2, 64, 128, (3, 8, 248), True, 0.8), {}),
+    "sparse_32": (_custom("sparse_32", 1, 2, 2, 64, 128, (3, 8, 256), True, 0.8), {}),
+    # sparsity 0 disables sparsity
+    "sparsity0": (_custom("sparsity0", 1, 2, 2, 128, 128, (9, 16, 32), True, 0.0), {}),
+    # no geometry at all: dense over a sequence that is not a multiple of 128
+    "no_grid": (_custom("no_grid", 1, 2, 2, 128, 1000, (0, 0, 0), False, 0.8), {"grid": (0, 0, 0)}),
+}
+
+
+def _inputs(w, layout):
+    if w.grid == (0, 0, 0):
+        rng_w = w.with_(grid=(1, 1, 1), prefix_len=w.prefix_len - 1)
+        q, k, v = make_qkv(rng_w)
+    else:
+        q, k, v = make_qkv(w)
+    if layout == "TND":
+        q, k, v = to_tnd(q), to_tnd(k), to_tnd(v)
+    return q, k, v
+
+
+def _desc(w, extra):
+    import block_sparse_video_rf_amd as rf
+    kw = dict(extra)
+    layout = kw.pop("layout", "BNSD")
+    if w.grid == (0, 0, 0):
+        return rf.Desc(batch=w.batch, heads_q=w.heads_q, heads_kv=w.heads_kv,
+                       head_dim=w.head_dim, seq_len=w.prefix_len, sparsity=w.sparsity,
+                       precision=w.precision, layout=layout)
+    return rf.Desc.from_workload(w, layout=layout, **kw)
+
+
+def _full_check(name):
+    w, extra = SMALL[name]
+    desc = _desc(w, extra)
+    layout = desc.layout
+    log(f"[case {name}] B={w.batch} N={w.heads_q}/{w.heads_kv} D={w.head_dim} S={desc.seq_len} "
+        f"grid={desc.grid} s={w.sparsity} {w.precision} {layout}")
+    q, k, v = _inputs(w, layout)
+    res = run_gpu(desc, q, k, v)
+    bufs = res["bufs"]
+    g = geometry_of(desc)
+    p = plan(g)
+    pi = permutation(g)
+    info = bufs.info
+    assert (info.n_blocks, info.n_sparse, info.topk) == (p.n_blocks, p.n_sparse, p.topk)
+    qb, kb, vb = (from_tnd(x, w.batch) if layout == "TND" else x for x in (q, k, v))
+
+    # Step 1: permuted copies and the block-transposed V, bit for bit.
+    if bufs.qp is not None:
+        assert np.array_equal(to_host_u16(bufs.qp), oracle.permute_rows(qb, pi))
+        assert np.array_equal(to_host_u16(bufs.kp), oracle.permute_rows(kb, pi))
+    vpt = to_host_u16(bufs.vpt)
+    assert np.array_equal(vpt, expected_vpt(oracle.permute_rows(vb, pi), p, w.head_dim))
+
+    ores = oracle.run(f32(q), f32(k), f32(v), g, precision=w.precision, layout=layout,
+                      batch=w.batch)
+    # Step 2: pooled means.
+    if not p.fallback:
+        qpool = bufs.q_pool.cpu().numpy()
+        kpool = bufs.k_pool.cpu().numpy()
+        assert np.abs(qpool - ores["q_pool"]).max() <= 2e-6
+        assert np.abs(kpool - ores["k_pool"]).max() <= 2e-6
+    # Mix: codes and scales, bit for bit.
+    if w.precision == "mix":
+        assert np.array_equal(bufs.q8.cpu().numpy(), ores["q8"])
+        assert np.array_equal(bufs.k8.cpu().numpy(), ores["k8"])
+        assert np.array_equal(bufs.q_scale.cpu().numpy(), ores["q_scale"])
+        assert np.array_equal(bufs.k_scale.cpu().numpy(), ores["k_scale"])
+    # Step 3: selection.
+    gi = bufs.select_idx.cpu().numpy()
+    gn = bufs.select_num.cpu().numpy()
+    swaps = check_selection(p, w.batch, w.heads_q, gi, gn, ores["scores"])
+    log(f"  selection: {swaps} near-tie rows")
+    # Step 4 + 5: attention with the GPU's own lists, through the inverse arrangement.
+    out = f32(to_host_u16(res["out"]))
+    ref_same_sel = oracle.run(f32(q), f32(k), f32(v), g, precision=w.precision, layout=layout,
+                              batch=w.batch, select=(gi, gn))["out"]
+    assert_close(out, ref_same_sel, BF16_TOL, "attention (GPU lists)")
+    tol = MIX_TOL if w.precision == "mix" else BF16_TOL
+    bf16_ref = ores["out"] if w.precision == "bf16" else oracle.run(
+        f32(q), f32(k), f32(v), g, layout=layout, batch=w.batch)["out"]
+    assert_close(out, bf16_ref, tol, "end to end vs bf16 oracle")
+    # Roundtrip: the inverse arrangement of the permuted Q is Q itself.
+    if bufs.qp is not None:
+        import torch
+        import block_sparse_video_rf_amd as rf
+        back = torch.empty_like(res["q"])
+        rf.rf_unpermute(desc, bufs.qp, back)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_u16(back), q)
+    return res, ores
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_case(name):
+    _full_check(name)
+
+
+def test_dense_cases_equal_dense_attention():
+    """Fallback and sparsity 0 lists are all dense, so the output is plain attention."""
+    import torch
+    for name in ("fallback_31", "sparsity0", "no_grid"):
+        w, extra = SMALL[name]
+        desc = _desc(w, extra)
+        q, k, v = _inputs(w, "BNSD")
+        res = run_gpu(desc, q, k, v)
+        assert res["bufs"].info.dense_fallback == 1
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            *(torch.from_numpy(f32(x).astype(np.float64)) for x in (q, k, v))).numpy()
+        assert_close(f32(to_host_u16(res["out"])), ref, BF16_TOL, f"{name} vs torch SDPA")
+
+
+def test_empty_lists_give_zeros():
+    """Sparsity 1, no prefix, no first frame, aligned grid: every list is empty."""
+    w = _custom("empty", 1, 2, 2, 128, 0, (4, 16, 16), False, 1.0)
+    import block_sparse_video_rf_amd as rf
+    desc = rf.Desc.from_workload(w, min_sparse_blocks=1)
+    q, k, v = make_qkv(w)
+    res = run_gpu(desc, q, k, v)
+    assert int(res["bufs"].select_num.max()) == 0
+    assert np.all(to_host_u16(res["out"]) == 0)
+
+
+def test_handmade_lists_skip_invalid_entries():
+    """rf_sparse_attn accepts any list: -1 and out-of-range ids are skipped, counts clamped."""
+    import torch
+    import block_sparse_video_rf_amd as rf
+    w, _ = SMALL["minimax_small"]
+    desc = rf.Desc.from_workload(w)
+    q, k, v = make_qkv(w)
+    res = run_gpu(desc, q, k, v)
+    b = res["bufs"]
+    nB = b.info.n_blocks
+    rng = np.random.default_rng(3)
+    idx = np.full((nB, w.heads_q, nB), -1, dtype=np.int32)
+    num = np.zeros((nB, w.heads_q), dtype=np.int32)
+    valid_idx = np.full_like(idx, -1)
+    valid_num = np.zeros_like(num)
+    for qb in range(nB):
+        for n in range(w.heads_q):
+            m = int(rng.integers(0, 12))
+            ids = rng.choice(nB, size=m, replace=False)
+            lst = list(ids) + [-1, nB + 5, 10 ** 6]
+            rng.shuffle(lst)
+            idx[qb, n, :len(lst)] = lst
+            num[qb, n] = len(lst) + (5 if qb % 7 == 0 else 0)  # some counts beyond max_kv... clamped
+            good = [x for x in lst if 0 <= x < nB]
+            valid_idx[qb, n, :len(good)] = good
+            valid_num[qb, n] = len(good)
+    num = np.minimum(num, nB)
+    out_p = torch.empty_like(b.out_p)
+    rf.rf_sparse_attn(desc, b.qp, b.kp, b.vpt, None, None, None, None,
+                      torch.from_numpy(idx).cuda(), torch.from_numpy(num).cuda(), nB, out_p)
+    torch.cuda.synchronize()
+    g = geometry_of(desc)
+    p = plan(g)
+    pi = permutation(g)
+    ref = oracle.sparse_attention(oracle.permute_rows(f32(q), pi), oracle.permute_rows(f32(k), pi),
+                                  oracle.permute_rows(f32(v), pi), p, valid_idx, valid_num,
+                                  1.0 / np.sqrt(w.head_dim))
+    assert_close(f32(to_host_u16(out_p)), ref, BF16_TOL, "handmade lists")
+
+
+def test_recomputed_pools_and_determinism():
+    """rf_pool_select without pooled inputs recomputes them; two runs are bit-identical."""
+    import torch
+    import block_sparse_video_rf_amd as rf
+    w, _ = SMALL["ragged_gqa"]
+    desc = rf.Desc.from_workload(w)
+    q, k, v = make_qkv(w)
+    r1 = run_gpu(desc, q, k, v)
+    r2 = run_gpu(desc, q, k, v)
+    assert torch.equal(r1["out"], r2["out"])
+    assert torch.equal(r1["bufs"].select_idx, r2["bufs"].select_idx)
+    b = r1["bufs"]
+    idx2 = torch.empty_like(b.select_idx)
+    num2 = torch.empty_like(b.select_num)
+    rf.rf_pool_select(desc, b.qp, b.kp, None, None, idx2, num2, b.info.n_blocks, b.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, b.select_idx) and torch.equal(num2, b.select_num)

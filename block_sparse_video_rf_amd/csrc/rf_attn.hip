@@ -1,10 +1,11 @@
 // Block-sparse attention: exact softmax(scale * Q K^T) V over the key blocks
 // listed in selectIdx ("aclnnRainFusionAttention", Formula; 128 x 128 blocks).
 //
-// One workgroup of 4 waves per (batch, query block, query head); wave w owns
-// query rows [32w, 32w + 32) of the block. The workgroup walks its list of
-// key blocks; for each it stages K (row-major, [128][D]) and V (already
-// block-transposed by the permute kernel, [D][128]) in LDS, then
+// One workgroup of 8 waves per (batch, query block, query head). Wave w owns
+// query rows [32 rg, 32 rg + 32) of the block (rg = w % 4) and one half of the
+// keys of every listed block (kh = w / 4). The workgroup walks its list of key
+// blocks, staging K (row-major, [128][D]) and V (already block-transposed by
+// the permute kernel, [D][128]) in LDS, and each wave computes
 //
 //   S^T = K Q^T  with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS,
 //                B = the wave's Q rows, held in registers for the whole walk)
@@ -22,6 +23,10 @@
 // contiguous, which is exactly the 8-value k-slice the PV product wants from
 // the B operand, and the matching V^T slice is one contiguous 16-byte LDS
 // read.
+//
+// The two waves on each SIMD (same rg) run half an iteration apart, so that
+// one issues matrix products while the other runs the softmax: the schedule
+// is described at the kernel.
 //
 // The mix precision replaces the QK^T operands by fp8 E4M3 codes
 // (v_mfma_scale_f32_32x32x64_f8f6f4, unit block scales) and folds
@@ -100,44 +105,193 @@ __device__ __forceinline__ void decode_wg(const RfGeom& g, int32_t w, int32_t* b
 // s_load, which neither waits on nor is waited on by the tile prefetches.
 typedef const int32_t __attribute__((address_space(4)))* list_ptr;
 
-// Next list position >= it holding a valid block id (or cnt). Uniform.
-__device__ __forceinline__ int next_valid(list_ptr list, int it, int cnt, int32_t nb) {
-  while (it < cnt) {
-    const int32_t j = list[it];
-    if (j >= 0 && j < nb) break;
-    ++it;
+// Scalar view of one float array (k_scale): uniform reads become s_load.
+typedef const float __attribute__((address_space(4)))* scale_ptr;
+
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
+// maxima (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Workgroup barrier that waits only for this wave's LDS operations: tile
+// prefetches from global memory stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Maxima without the NaN canonicalisation fmaxf needs (no NaN reaches them:
+// masked scores are -inf).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// Maximum of a lane's value and that of lane l ^ 32 (v_permlane32_swap hands
+// every lane its own value and its partner's).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max3f(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
+}
+
+// Operand schedule of one MFMA interval: the S^T products of this block
+// (A = K rows from LDS) followed by the O^T products of the previous block
+// (A = V^T rows from LDS). Every LDS read is one 16-byte fragment per lane;
+// an fp8 S^T product takes two.
+template <int D, bool MIX>
+struct MfmaPlan {
+  static constexpr int DT = D / 32;
+  static constexpr int QK_STEPS = MIX ? D / 64 : D / 16;
+  static constexpr int S_RPM = MIX ? 2 : 1;          // reads per S^T product
+  static constexpr int NS_MFMA = 2 * QK_STEPS;       // S^T products (2 key tiles)
+  static constexpr int NS_READ = NS_MFMA * S_RPM;
+  static constexpr int NPV = 4 * DT;                 // O^T products (4 k-steps x DT tiles)
+  static constexpr int NREAD = NS_READ + NPV;
+  static constexpr int NMFMA = NS_MFMA + NPV;
+  static constexpr int NR = 8;                       // fragments in flight
+  static constexpr int NPRE = NR < NS_READ ? NR : NS_READ;  // K reads issued before the barrier
+  static constexpr int rend(int m) { return m < NS_MFMA ? (m + 1) * S_RPM : NS_READ + (m - NS_MFMA) + 1; }
+};
+
+// Ring of fragments in named registers (an array could be placed in scratch).
+struct FragRing {
+  uint4 r0, r1, r2, r3, r4, r5, r6, r7;
+};
+template <int I>
+__device__ __forceinline__ uint4& ring_slot(FragRing& f) {
+  static_assert(I >= 0 && I < 8, "ring slot");
+  if constexpr (I == 0) return f.r0;
+  else if constexpr (I == 1) return f.r1;
+  else if constexpr (I == 2) return f.r2;
+  else if constexpr (I == 3) return f.r3;
+  else if constexpr (I == 4) return f.r4;
+  else if constexpr (I == 5) return f.r5;
+  else if constexpr (I == 6) return f.r6;
+  else return f.r7;
+}
+
+template <int D, bool MIX>
+struct MfmaCtx {
+  using P = MfmaPlan<D, MIX>;
+  const uint8_t* kbase;  // this lane's first K fragment in the current K buffer
+  const uint8_t* vbase;  // this lane's first V^T fragment in the previous block's buffer
+  FragRing ring;
+  f32x16 s[2];
+  f32x16 o[P::DT];
+  bf16x8 qf[MIX ? 1 : P::QK_STEPS];
+  i32x8 qf8[MIX ? P::QK_STEPS : 1];
+  bf16x8 pf16[2][2];
+};
+
+// LDS byte offset of read R relative to its base (compile-time).
+template <int D, bool MIX, int R>
+__device__ __forceinline__ const uint8_t* read_addr(const MfmaCtx<D, MIX>& c) {
+  using P = MfmaPlan<D, MIX>;
+  constexpr int KSTR = (MIX ? D : 2 * D) + 16;
+  constexpr int VSTR = 256 + 16;
+  if constexpr (R < P::NS_READ) {
+    constexpr int sm = R / P::S_RPM, half = R % P::S_RPM, st = sm / 2, t = sm % 2;
+    return c.kbase + 32 * t * KSTR + (MIX ? 64 * st + 16 * half : 32 * st);
+  } else {
+    constexpr int pm = R - P::NS_READ, tu = pm / P::DT, e = pm % P::DT;
+    return c.vbase + 32 * e * VSTR + 2 * (32 * (tu / 2) + 16 * (tu % 2));
   }
-  return it;
+}
+
+template <int D, bool MIX, int R, int END>
+__device__ __forceinline__ void issue_reads(MfmaCtx<D, MIX>& c) {
+  using P = MfmaPlan<D, MIX>;
+  if constexpr (R < END && R < P::NREAD) {
+    ring_slot<R % P::NR>(c.ring) = *reinterpret_cast<const uint4*>(read_addr<D, MIX, R>(c));
+    issue_reads<D, MIX, R + 1, END>(c);
+  }
+}
+
+template <int D, bool MIX, int M, int MEND = MfmaPlan<D, MIX>::NMFMA>
+__device__ __forceinline__ void mfma_steps(MfmaCtx<D, MIX>& c) {
+  using P = MfmaPlan<D, MIX>;
+  if constexpr (M < MEND) {
+    if constexpr (M < P::NS_MFMA) {
+      constexpr int st = M / 2, t = M % 2;
+      if constexpr (MIX) {
+        constexpr int r = 2 * M;
+        const uint4 x0 = ring_slot<r % P::NR>(c.ring), x1 = ring_slot<(r + 1) % P::NR>(c.ring);
+        const i32x8 ka = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                          (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        c.s[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, c.qf8[st], c.s[t], 0, 0, 0,
+                                                                 127, 0, 127);
+      } else {
+        bf16x8 ka;
+        __builtin_memcpy(&ka, &ring_slot<M % P::NR>(c.ring), 16);
+        c.s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, c.qf[st], c.s[t], 0, 0, 0);
+      }
+    } else {
+      constexpr int pm = M - P::NS_MFMA, tu = pm / P::DT, e = pm % P::DT;
+      constexpr int r = P::NS_READ + pm;
+      bf16x8 va;
+      __builtin_memcpy(&va, &ring_slot<r % P::NR>(c.ring), 16);
+      c.o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, c.pf16[tu / 2][tu % 2], c.o[e], 0, 0, 0);
+    }
+    // Refill the slots this product consumed: NR reads stay ahead.
+    constexpr int done_before = M == 0 ? 0 : P::rend(M - 1);
+    issue_reads<D, MIX, done_before + P::NR, P::rend(M) + P::NR>(c);
+    // Keep this order: the scheduler would otherwise pull each read down to
+    // its use and leave too few in flight.
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_steps<D, MIX, M + 1, MEND>(c);
+  }
 }
 
 // Workgroup of 8 waves per (batch, query block, head). Wave w owns query rows
 // [32 rg, 32 rg + 32) with rg = w % 4 and key rows [64 kh, 64 kh + 64) of every
 // listed block with kh = w / 4: each wave keeps its own running max / sum /
 // O^T over its half of the keys, and the two halves are merged through LDS at
-// the end (exact: the merge rescales both to the common maximum). Two waves
-// per SIMD from one workgroup let one wave's softmax overlap the other's MFMA.
+// the end (exact: the merge rescales both to the common maximum).
 //
-// The next block's K and V^T tiles are fetched into registers while the
-// current block is computed, then written to LDS between two barriers: the
-// global-memory latency hides behind a whole block of work.
+// The two waves that share a SIMD (same rg) run half an iteration apart: the
+// kh = 1 group starts one barrier interval late. Each iteration of a wave is
+//   MFMA interval: S^T = K Q^T of this block, O^T += V^T P^T of the previous
+//                  one, and the global loads of one tile into registers
+//   VALU interval: that tile stored to LDS, the softmax of this block's S^T
+//                  into P
+// so in every interval one wave of each SIMD issues matrix work while the
+// other runs the softmax. The MFMA interval streams its LDS operands through
+// a ring of fragments kept several reads ahead (the first reads, K of the next
+// block, are issued before the barrier that opens it) and spreads its global
+// loads between the products. K and V^T tiles are double buffered in LDS: the
+// kh = 0 waves copy V^T of the block they are scoring, the kh = 1 waves K of
+// the block two ahead.
+//
+// Barriers wait only for LDS operations (lds_barrier), and the block ids come
+// from a window of list entries held in scalar registers, so no wait in the
+// loop covers anything but the data it needs.
 template <int D, bool MIX>
 __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
-  constexpr int KSTR = MIX ? D + 16 : 2 * D + 16;  // K row stride in LDS (bytes, padded)
-  constexpr int VSTR = 256 + 16;                   // V^T row stride in LDS (bytes, padded)
-  constexpr int DT = D / 32;                       // 32-wide channel tiles of O^T
-  constexpr int KCH = (MIX ? D : 2 * D) / 16;      // 16-byte chunks per K row
-  constexpr int K_PER_T = 128 * KCH / kThreads8;   // K chunks staged per thread
-  constexpr int V_PER_T = D * 16 / kThreads8;      // V^T chunks staged per thread
-  constexpr int TILE_BYTES = 128 * KSTR + D * VSTR;
+  using PL = MfmaPlan<D, MIX>;
+  constexpr int KROW = MIX ? D : 2 * D;  // K row bytes in global memory
+  constexpr int KSTR = KROW + 16;        // K row stride in LDS (bytes, padded)
+  constexpr int VSTR = 256 + 16;         // V^T row stride in LDS (bytes, padded)
+  constexpr int DT = D / 32;             // 32-wide channel tiles of O^T
+  constexpr int KCH = KROW / 16;         // 16-byte chunks per K row
+  constexpr int K_CH = 128 * KCH / 256;  // K chunks per thread of the kh = 1 group
+  constexpr int V_CH = D * 16 / 256;     // V^T chunks per thread of the kh = 0 group
+  constexpr int NSTG = K_CH > V_CH ? K_CH : V_CH;
+  constexpr int KT = 128 * KSTR, VT = D * VSTR;
+  constexpr int TILE_BYTES = 2 * KT + 2 * VT;
   constexpr int MERGE_BYTES = 4 * (DT * 16 + 2) * 64 * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES];
-  uint8_t* ks = smem;
-  uint8_t* vs = smem + 128 * KSTR;
+  static_assert(MERGE_BYTES <= TILE_BYTES, "merge buffer");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[TILE_BYTES];
+  uint8_t* const kbuf0 = smem;
+  uint8_t* const vbuf0 = smem + 2 * KT;
 
   const RfGeom& g = a.g;
   const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64, li = lane % 32, h = lane / 32;
+  // The wave index is uniform; readfirstlane lets the compiler see that, so
+  // branches on kh are scalar branches.
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64, li = lane % 32, h = lane / 32;
   const int rg = wave & 3, kh = wave >> 2;
+  const int gt = tid & 255;  // thread index within its kh group
   int32_t b, q, n;
   decode_wg(g, blockIdx.x, &b, &q, &n);
   const int32_t nk = n / g.G;
@@ -147,40 +301,44 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   const int qrow = 32 * rg + li;
   const bool qvalid = qrow < len;
 
+  MfmaCtx<D, MIX> c;
   // Q fragment (B operand of S^T = K Q^T): query row qrow, channels by k-step.
-  constexpr int QK_STEPS = MIX ? D / 64 : D / 16;
-  bf16x8 qf[MIX ? 1 : QK_STEPS];
-  i32x8 qf8[MIX ? QK_STEPS : 1];
   float q_sigma = 1.0f;
   if constexpr (MIX) {
     const uint8_t* qr = a.q8 + (((int64_t)b * g.N1 + n) * g.S + row0 + qrow) * D;
 #pragma unroll
-    for (int st = 0; st < QK_STEPS; ++st) {
+    for (int st = 0; st < PL::QK_STEPS; ++st) {
       if (qvalid) {
         const uint4 x0 = *reinterpret_cast<const uint4*>(qr + 64 * st + 32 * h);
         const uint4 x1 = *reinterpret_cast<const uint4*>(qr + 64 * st + 32 * h + 16);
-        qf8[st] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                        (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        c.qf8[st] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                          (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
       } else {
-        qf8[st] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        c.qf8[st] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
       }
     }
     q_sigma = a.q_scale[((int64_t)b * g.N1 + n) * g.n_blocks + q];
   } else {
     const uint16_t* qr = a.qp + (((int64_t)b * g.N1 + n) * g.S + row0 + qrow) * D;
 #pragma unroll
-    for (int st = 0; st < QK_STEPS; ++st) {
+    for (int st = 0; st < PL::QK_STEPS; ++st) {
       if (qvalid) {
-        qf[st] = *reinterpret_cast<const bf16x8*>(qr + 16 * st + 8 * h);
+        c.qf[st] = *reinterpret_cast<const bf16x8*>(qr + 16 * st + 8 * h);
       } else {
-        qf[st] = bf16x8{};
+        c.qf[st] = bf16x8{};
       }
     }
   }
+  // Let the Q loads land here: otherwise the wait for them stays inside the
+  // loop, where it would also wait for the in-flight tile prefetches.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-  f32x16 o[DT];
 #pragma unroll
-  for (int e = 0; e < DT; ++e) o[e] = f32x16{};
+  for (int e = 0; e < DT; ++e) c.o[e] = f32x16{};
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) c.pf16[t][u] = bf16x8{};
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int64_t sel_row = ((int64_t)b * g.n_blocks + q) * g.N1 + n;
@@ -193,121 +351,187 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
           : reinterpret_cast<const uint8_t*>(a.kp + ((int64_t)b * g.N2 + nk) * g.S * D);
   const uint8_t* vbytes = reinterpret_cast<const uint8_t*>(
       a.vpt + ((int64_t)b * g.N2 + nk) * g.n_blocks * (int64_t)D * 128);
-  const float* kscale = MIX ? a.k_scale + ((int64_t)b * g.N2 + nk) * g.n_blocks : nullptr;
+  const scale_ptr kscale =
+      MIX ? (scale_ptr)(a.k_scale + ((int64_t)b * g.N2 + nk) * g.n_blocks) : nullptr;
 
-  // Register staging of one block's K rows and V^T rows. Rows past a short
-  // block's end re-read its last row (always in bounds, no branch); they are
-  // masked out of the softmax.
-  // (Named registers rather than arrays: they must never live in scratch.)
-  static_assert(K_PER_T >= 1 && K_PER_T <= 4 && V_PER_T >= 1 && V_PER_T <= 4, "staging size");
-  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
-#define RF_KLD(VAR, M)                                                                     \
-  if constexpr ((M) < K_PER_T) {                                                           \
-    const int slot_ = (M) * kThreads8 + tid, r_ = slot_ / KCH, c_ = slot_ % KCH;           \
+  // Tile copies through registers. K rows past a short block's end re-read its
+  // last row (always in bounds, no branch); they are masked out of the softmax.
+  // (Named registers rather than an array: they must never live in scratch.)
+  static_assert(NSTG <= 8, "staging size");
+  uint4 st0, st1, st2, st3, st4, st5, st6, st7;
+#define RF_KLD1(VAR, M)                                                                    \
+  if constexpr ((M) < K_CH) {                                                              \
+    const int slot_ = (M) * 256 + gt, r_ = slot_ / KCH, c_ = slot_ % KCH;                  \
     const int rr_ = r_ < flen_ ? r_ : flen_ - 1;                                           \
-    VAR = *reinterpret_cast<const uint4*>(ksrc_ + rr_ * (MIX ? D : 2 * D) + c_ * 16);      \
+    VAR = *reinterpret_cast<const uint4*>(src_ + rr_ * KROW + c_ * 16);                    \
   }
-#define RF_VLD(VAR, M)                                                                     \
-  if constexpr ((M) < V_PER_T) VAR = *reinterpret_cast<const uint4*>(vsrc_ + ((M) * kThreads8 + tid) * 16);
-#define RF_FETCH(J)                                                                        \
+#define RF_KST1(BUF, VAR, M)                                                               \
+  if constexpr ((M) < K_CH) {                                                              \
+    const int slot_ = (M) * 256 + gt, r_ = slot_ / KCH, c_ = slot_ % KCH;                  \
+    *reinterpret_cast<uint4*>((BUF) + r_ * KSTR + c_ * 16) = VAR;                          \
+  }
+#define RF_VLD1(VAR, M)                                                                    \
+  if constexpr ((M) < V_CH) VAR = *reinterpret_cast<const uint4*>(src_ + ((M) * 256 + gt) * 16);
+#define RF_VST1(BUF, VAR, M)                                                               \
+  if constexpr ((M) < V_CH) {                                                              \
+    const int slot_ = (M) * 256 + gt, d_ = slot_ / 16, c_ = slot_ % 16;                    \
+    *reinterpret_cast<uint4*>((BUF) + d_ * VSTR + c_ * 16) = VAR;                          \
+  }
+#define RF_LOAD_K(J)                                                                       \
   do {                                                                                     \
     int64_t fr0_;                                                                          \
     int32_t flen_;                                                                         \
     rf_block_rows(g, (J), &fr0_, &flen_);                                                  \
-    const uint8_t* ksrc_ = kbytes + fr0_ * (MIX ? D : 2 * D);                              \
-    const uint8_t* vsrc_ = vbytes + (int64_t)(J) * D * 256;                                \
-    RF_KLD(k0, 0) RF_KLD(k1, 1) RF_KLD(k2, 2) RF_KLD(k3, 3)                                \
-    RF_VLD(v0, 0) RF_VLD(v1, 1) RF_VLD(v2, 2) RF_VLD(v3, 3)                                \
+    const uint8_t* src_ = kbytes + fr0_ * KROW;                                            \
+    RF_KLD1(st0, 0) RF_KLD1(st1, 1) RF_KLD1(st2, 2) RF_KLD1(st3, 3)                        \
+    RF_KLD1(st4, 4) RF_KLD1(st5, 5) RF_KLD1(st6, 6) RF_KLD1(st7, 7)                        \
   } while (0)
-#define RF_KST(VAR, M)                                                                     \
-  if constexpr ((M) < K_PER_T) {                                                           \
-    const int slot_ = (M) * kThreads8 + tid, r_ = slot_ / KCH, c_ = slot_ % KCH;           \
-    *reinterpret_cast<uint4*>(ks + r_ * KSTR + c_ * 16) = VAR;                             \
-  }
-#define RF_VST(VAR, M)                                                                     \
-  if constexpr ((M) < V_PER_T) {                                                           \
-    const int slot_ = (M) * kThreads8 + tid, d_ = slot_ / 16, c_ = slot_ % 16;             \
-    *reinterpret_cast<uint4*>(vs + d_ * VSTR + c_ * 16) = VAR;                             \
-  }
-#define RF_STASH()                                                                         \
+#define RF_STORE_K(BUF)                                                                    \
   do {                                                                                     \
-    RF_KST(k0, 0) RF_KST(k1, 1) RF_KST(k2, 2) RF_KST(k3, 3)                                \
-    RF_VST(v0, 0) RF_VST(v1, 1) RF_VST(v2, 2) RF_VST(v3, 3)                                \
+    RF_KST1(BUF, st0, 0) RF_KST1(BUF, st1, 1) RF_KST1(BUF, st2, 2) RF_KST1(BUF, st3, 3)    \
+    RF_KST1(BUF, st4, 4) RF_KST1(BUF, st5, 5) RF_KST1(BUF, st6, 6) RF_KST1(BUF, st7, 7)    \
+  } while (0)
+#define RF_LOAD_V(J)                                                                       \
+  do {                                                                                     \
+    const uint8_t* src_ = vbytes + (int64_t)(J) * D * 256;                                 \
+    RF_VLD1(st0, 0) RF_VLD1(st1, 1) RF_VLD1(st2, 2) RF_VLD1(st3, 3)                        \
+    RF_VLD1(st4, 4) RF_VLD1(st5, 5) RF_VLD1(st6, 6) RF_VLD1(st7, 7)                        \
+  } while (0)
+#define RF_STORE_V(BUF)                                                                    \
+  do {                                                                                     \
+    RF_VST1(BUF, st0, 0) RF_VST1(BUF, st1, 1) RF_VST1(BUF, st2, 2) RF_VST1(BUF, st3, 3)    \
+    RF_VST1(BUF, st4, 4) RF_VST1(BUF, st5, 5) RF_VST1(BUF, st6, 6) RF_VST1(BUF, st7, 7)    \
   } while (0)
 
-  int it = next_valid(list, 0, cnt, g.n_blocks);
-  if (it < cnt) {
-    RF_FETCH(list[it]);
-    RF_STASH();
-  }
-  __syncthreads();
+  // Block ids come from a window of four list entries in scalar registers
+  // (blocks i .. i + 3); the entry four ahead is loaded one iteration early.
+  // An entry outside [0, n_blocks) is processed as a fully masked block
+  // (block 0's tiles with no valid key), which adds exactly nothing: the same
+  // as skipping it. Entries past the list end stand for block 0 too; nothing
+  // reads what is fetched for them.
+  const int32_t nbk = g.n_blocks;
+  auto entry = [&](int pos) -> int32_t { return pos < cnt ? list[pos] : -1; };
+  auto safe = [&](int32_t jr) -> int32_t { return (jr >= 0 && jr < nbk) ? jr : 0; };
+  int32_t w0 = entry(0), w1 = entry(1), w2 = entry(2), w3 = entry(3);
 
-  const int krow = 64 * kh + kappa(li);  // this lane's K row in tile t: krow + 32 t
-  while (it < cnt) {
-    const int32_t j = list[it];
+  // Prologue: K of blocks 0 and 1 to LDS. The V^T buffer that
+  // the first (empty) PV product reads is zeroed: P is zero there, and
+  // 0 * (stale bits) could be NaN.
+  if (cnt > 0) {
+    if (kh == 0) {
+      RF_LOAD_K(safe(w0));
+      RF_STORE_K(kbuf0);
+    } else {
+      RF_LOAD_K(safe(w1));
+      RF_STORE_K(kbuf0 + KT);
+    }
+    for (int x = tid; x < VT / 16; x += kThreads8)
+      reinterpret_cast<uint4*>(vbuf0 + VT)[x] = uint4{0, 0, 0, 0};
+  }
+  lds_barrier();
+  if (kh == 1) lds_barrier();  // the kh = 1 group runs one interval behind
+
+  // This lane's fragment bases: K row 64 kh + kappa(li) (+ 32 t), V^T row li
+  // (+ 32 e) at key column 64 kh + 8 h (+ 16 k-step).
+  const int koff = (64 * kh + kappa(li)) * KSTR + (MIX ? 32 * h : 16 * h);
+  const int voff = li * VSTR + 2 * (64 * kh + 8 * h);
+  int par = 0;  // parity of block i: its K tile sits in K buffer par
+  c.kbase = kbuf0 + koff;
+  issue_reads<D, MIX, 0, PL::NPRE>(c);
+  for (int i = 0; i < cnt; ++i) {
+    const int32_t j = safe(w0);
     int64_t kr0;
     int32_t klen;
     rf_block_rows(g, j, &kr0, &klen);
-    const int nx = next_valid(list, it + 1, cnt, g.n_blocks);
-    // Next block's tiles are in flight during this block's work (the last
-    // iteration re-fetches its own block, which nothing reads afterwards).
-    RF_FETCH(nx < cnt ? list[nx] : j);
+    if (w0 != j) klen = 0;
+    // The tile this group loads in this MFMA interval and stores in the VALU
+    // interval that follows: V^T of block i, or K of block i + 2.
+    const int32_t jcopy = kh == 0 ? j : safe(w2);
 
-    // S^T tiles: s[t] covers key rows 64 kh + [32t, 32t + 32) of the block.
-    f32x16 s[2];
+    // ---- MFMA interval ----
+    c.vbase = vbuf0 + (par ^ 1) * VT + voff;  // V^T of the previous block
 #pragma unroll
-    for (int t = 0; t < 2; ++t) s[t] = f32x16{};
-    if constexpr (MIX) {
-#pragma unroll
-      for (int st = 0; st < QK_STEPS; ++st) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const uint8_t* kr = ks + (krow + 32 * t) * KSTR + 64 * st + 32 * h;
-          const uint4 x0 = *reinterpret_cast<const uint4*>(kr);
-          const uint4 x1 = *reinterpret_cast<const uint4*>(kr + 16);
-          const i32x8 ka = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                            (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-          s[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qf8[st], s[t], 0, 0, 0, 127,
-                                                                 0, 127);
-        }
-      }
+    for (int t = 0; t < 2; ++t) c.s[t] = f32x16{};
+    issue_reads<D, MIX, PL::NPRE, PL::NR>(c);
+    // The next tile's global loads ride along with the products, one after
+    // every NMFMA / 8 of them, so that no wave stalls on a burst of loads.
+    {
+      int64_t fr0_;
+      int32_t flen_;
+      rf_block_rows(g, jcopy, &fr0_, &flen_);
+      const uint8_t* const ksrc_ = kbytes + fr0_ * KROW;
+      const uint8_t* const vsrc_ = vbytes + (int64_t)jcopy * D * 256;
+#define RF_LD(M)                                                                           \
+  if (kh == 0) {                                                                           \
+    const uint8_t* src_ = vsrc_;                                                           \
+    RF_VLD1(st##M, M)                                                                      \
+  } else {                                                                                 \
+    const uint8_t* src_ = ksrc_;                                                           \
+    RF_KLD1(st##M, M)                                                                      \
+  }
+#define RF_Q(K) ((K) * PL::NMFMA / 8)
+      mfma_steps<D, MIX, 0, RF_Q(1)>(c);
+      RF_LD(0)
+      mfma_steps<D, MIX, RF_Q(1), RF_Q(2)>(c);
+      RF_LD(1)
+      mfma_steps<D, MIX, RF_Q(2), RF_Q(3)>(c);
+      RF_LD(2)
+      mfma_steps<D, MIX, RF_Q(3), RF_Q(4)>(c);
+      RF_LD(3)
+      mfma_steps<D, MIX, RF_Q(4), RF_Q(5)>(c);
+      RF_LD(4)
+      mfma_steps<D, MIX, RF_Q(5), RF_Q(6)>(c);
+      RF_LD(5)
+      mfma_steps<D, MIX, RF_Q(6), RF_Q(7)>(c);
+      RF_LD(6)
+      mfma_steps<D, MIX, RF_Q(7), RF_Q(8)>(c);
+      RF_LD(7)
+#undef RF_LD
+#undef RF_Q
+    }
+    lds_barrier();
+
+    // ---- VALU interval ----
+    // Next window entry (consumed after the closing barrier).
+    const int32_t w4 = entry(i + 4 < cnt ? i + 4 : cnt);
+    // Tile copy: the staged tile to LDS, then the next one into registers.
+    if (kh == 0) {
+      // V^T of block i into buffer par (read in the next two intervals).
+      RF_STORE_V(vbuf0 + par * VT);
     } else {
-#pragma unroll
-      for (int st = 0; st < QK_STEPS; ++st) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + (krow + 32 * t) * KSTR +
-                                                             32 * st + 16 * h);
-          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s[t], 0, 0, 0);
-        }
-      }
+      // K of block i + 2 into buffer par (block i's K was last read in the
+      // MFMA interval just done).
+      RF_STORE_K(kbuf0 + par * KT);
     }
 
-    // Mask rows past a short block's end.
+    // Mask rows past a short block's end (all rows of a masked block).
     if (klen < 128) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int kv = 64 * kh + 32 * t + 16 * (v / 8) + 8 * h + (v % 8);
-          if (kv >= klen) s[t][v] = -INFINITY;
+          if (kv >= klen) c.s[t][v] = -INFINITY;
         }
     }
 
-    float c = a.scale_log2;
-    if constexpr (MIX) c *= q_sigma * kscale[j];
+    float cs = a.scale_log2;
+    if constexpr (MIX) cs *= q_sigma * kscale[j];
 
     // Maximum over this wave's keys of the row (then the partner half-wave).
-    float mx = -INFINITY;
+    float m0 = c.s[0][0], m1 = c.s[1][0];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[t][v], s[t][v + 1]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int v = 1; v < 15; v += 2) {
+      m0 = max3f(m0, c.s[0][v], c.s[0][v + 1]);
+      m1 = max3f(m1, c.s[1][v], c.s[1][v + 1]);
+    }
+    const float mx = max_halves(max3f(m0, m1, max3f(c.s[0][15], c.s[1][15], c.s[1][15])));
     // The reference maximum m_run only moves when the block exceeds it by more
     // than 8 (log2 units): exponentials stay <= 2^8, which bf16 P and fp32 sums
-    // hold as well, and the rescale of O is skipped for most blocks.
-    const float mc = mx * c;
+    // hold as well, and the rescale of O is skipped for most blocks. O^T holds
+    // every product up to the previous block here, exactly what the rescale
+    // must cover.
+    const float mc = mx * cs;
     if (__any(mc > m_run + 8.0f)) {
       const float m_new = fmaxf(m_run, mc);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -316,27 +540,38 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < DT; ++e)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[e][v] *= alpha;
+        for (int v = 0; v < 16; ++v) c.o[e][v] *= alpha;
     }
     // While every key so far is masked m_run is -inf; any finite stand-in keeps
     // exp2(-inf - m) at 0 instead of NaN.
     const float mneg = -fmaxf(m_run, -1e30f);
 
     float lsum = 0.0f;
-    bf16x8 pf[2][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[t][8 * u + m], c, mneg));
+          const float p = __builtin_amdgcn_exp2f(fmaf(c.s[t][8 * u + m], cs, mneg));
           lsum += p;
-          pf[t][u][m] = (__bf16)p;
+          c.pf16[t][u][m] = (__bf16)p;
         }
     l_run += lsum;
 
-    // O^T += V^T P^T over this wave's 64 key rows (4 k-steps of 16).
+    // First K fragments of block i + 1 (written at least one interval ago).
+    par ^= 1;
+    c.kbase = kbuf0 + par * KT + koff;
+    issue_reads<D, MIX, 0, PL::NPRE>(c);
+    lds_barrier();
+    w0 = w1;
+    w1 = w2;
+    w2 = w3;
+    w3 = w4;
+  }
+  // O^T += V^T P^T of the last block.
+  if (cnt > 0) {
+    const uint8_t* vs = vbuf0 + (par ^ 1) * VT + voff;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -344,30 +579,29 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < DT; ++e) {
           const bf16x8 va = *reinterpret_cast<const bf16x8*>(
-              vs + (32 * e + li) * VSTR + 2 * (64 * kh + 32 * t + 16 * u + 8 * h));
-          o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[t][u], o[e], 0, 0, 0);
+              vs + 32 * e * VSTR + 2 * (32 * t + 16 * u));
+          c.o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, c.pf16[t][u], c.o[e], 0, 0, 0);
         }
-
-    __syncthreads();  // every wave is done with this block's tiles
-    RF_STASH();
-    __syncthreads();
-    it = nx;
   }
+  if (kh == 0) lds_barrier();  // matches the kh = 1 group's extra barrier
 
-#undef RF_FETCH
-#undef RF_STASH
-#undef RF_KLD
-#undef RF_VLD
-#undef RF_KST
-#undef RF_VST
+#undef RF_LOAD_K
+#undef RF_STORE_K
+#undef RF_LOAD_V
+#undef RF_STORE_V
+#undef RF_KLD1
+#undef RF_KST1
+#undef RF_VLD1
+#undef RF_VST1
 
+  __syncthreads();  // every wave is done with the tiles
   // Merge the two key halves: wave (rg, 1) hands its state to wave (rg, 0).
   float* mbuf = reinterpret_cast<float*>(smem) + rg * (DT * 16 + 2) * 64;
   if (kh == 1) {
 #pragma unroll
     for (int e = 0; e < DT; ++e)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mbuf[(e * 16 + v) * 64 + lane] = o[e][v];
+      for (int v = 0; v < 16; ++v) mbuf[(e * 16 + v) * 64 + lane] = c.o[e][v];
     mbuf[DT * 16 * 64 + lane] = m_run;
     mbuf[(DT * 16 + 1) * 64 + lane] = l_run;
   }
@@ -392,7 +626,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int v = 4 * a4 + x;
-          r[x] = (__bf16)((o[e][v] * a0 + mbuf[(e * 16 + v) * 64 + lane] * a1) * inv);
+          r[x] = (__bf16)((c.o[e][v] * a0 + mbuf[(e * 16 + v) * 64 + lane] * a1) * inv);
         }
         uint2 w;
         __builtin_memcpy(&w, r, 8);

@@ -187,7 +187,8 @@ rf_status rf_pool_select(const rf_desc* desc, const void* qp, const void* kp,
  * bf16 precision reads qp, kp, vpt; mix precision reads q8, k8, q_scale,
  * k_scale, vpt (logits = scale * q_scale * k_scale * <q8, k8>).
  * select_idx / select_num as above (any list the caller builds is accepted:
- * entries outside [0, n_blocks) are skipped, counts are clamped to max_kv).
+ * entries outside [0, n_blocks) contribute nothing, exactly as if skipped,
+ * provided V holds finite values; counts are clamped to max_kv).
  * A row with an empty list gets zeros.
  * out_p: bf16 [B, N1, S, D], permuted row order, rounded to nearest even. */
 rf_status rf_sparse_attn(const rf_desc* desc, const void* qp, const void* kp, const void* vpt,

@@ -45,6 +45,9 @@ rf_status rf_derive(const rf_desc* d, RfGeom* g, rf_plan_info* info) {
   if (d->precision != RF_PREC_BF16 && d->precision != RF_PREC_MIX) return RF_ERR_PRECISION;
   // Per-(batch, head) row offsets are formed in 64-bit; keep counts in 32-bit ranges.
   if (d->seq_len > ((int64_t)1 << 31) - 128) return RF_ERR_SHAPE;
+  // The attention kernel addresses one (batch, kv head)'s K and V^T with
+  // 32-bit byte offsets: seq_len * head_dim * 2 bytes must stay below 2^31.
+  if (d->seq_len * (int64_t)d->head_dim * 2 > 0x7fffffff) return RF_ERR_SHAPE;
   if ((int64_t)d->batch * d->heads_q > 65535 || (int64_t)d->batch * d->heads_kv > 65535)
     return RF_ERR_SHAPE;
 

@@ -45,6 +45,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct AttnArgs {
   RfGeom g;
@@ -111,6 +112,13 @@ typedef const float __attribute__((address_space(4)))* scale_ptr;
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
 // maxima (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Raw buffer descriptor over [base, base + bytes): a load past the end
+// returns zeros. (Third dword: the raw 32-bit data format used for plain
+// byte-addressed buffers on gfx9.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 // Workgroup barrier that waits only for this wave's LDS operations: tile
 // prefetches from global memory stay in flight across it.
@@ -354,48 +362,49 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   const scale_ptr kscale =
       MIX ? (scale_ptr)(a.k_scale + ((int64_t)b * g.N2 + nk) * g.n_blocks) : nullptr;
 
-  // Tile copies through registers. K rows past a short block's end re-read its
-  // last row (always in bounds, no branch); they are masked out of the softmax.
+  // Tile copies: buffer loads over this (batch, kv head)'s K and V^T.
+  const __amdgpu_buffer_rsrc_t rk = raw_buffer(kbytes, (uint32_t)(g.S * KROW));
+  const __amdgpu_buffer_rsrc_t rv = raw_buffer(vbytes, (uint32_t)((int64_t)g.n_blocks * D * 256));
+  auto k_tile_off = [&](int32_t jb) -> int {
+    int64_t r0;
+    int32_t fl;
+    rf_block_rows(g, jb, &r0, &fl);
+    return (int)(r0 * KROW);
+  };
+  // K rows past a short block's end are whatever follows in memory (zeros past
+  // the end of K); they are masked out of the softmax.
   // (Named registers rather than an array: they must never live in scratch.)
   static_assert(NSTG <= 8, "staging size");
-  uint4 st0, st1, st2, st3, st4, st5, st6, st7;
-#define RF_KLD1(VAR, M)                                                                    \
-  if constexpr ((M) < K_CH) {                                                              \
-    const int slot_ = (M) * 256 + gt, r_ = slot_ / KCH, c_ = slot_ % KCH;                  \
-    const int rr_ = r_ < flen_ ? r_ : flen_ - 1;                                           \
-    VAR = *reinterpret_cast<const uint4*>(src_ + rr_ * KROW + c_ * 16);                    \
+  u32x4 st0, st1, st2, st3, st4, st5, st6, st7;
+#define RF_GLD1(VAR, M)                                                                    \
+  if constexpr ((M) < NSTG) {                                                              \
+    if ((M) < nch_) VAR = __builtin_amdgcn_raw_buffer_load_b128(rs_, gt * 16, so_ + (M) * 4096, 0); \
   }
 #define RF_KST1(BUF, VAR, M)                                                               \
   if constexpr ((M) < K_CH) {                                                              \
     const int slot_ = (M) * 256 + gt, r_ = slot_ / KCH, c_ = slot_ % KCH;                  \
-    *reinterpret_cast<uint4*>((BUF) + r_ * KSTR + c_ * 16) = VAR;                          \
+    *reinterpret_cast<u32x4*>((BUF) + r_ * KSTR + c_ * 16) = VAR;                          \
   }
-#define RF_VLD1(VAR, M)                                                                    \
-  if constexpr ((M) < V_CH) VAR = *reinterpret_cast<const uint4*>(src_ + ((M) * 256 + gt) * 16);
 #define RF_VST1(BUF, VAR, M)                                                               \
   if constexpr ((M) < V_CH) {                                                              \
     const int slot_ = (M) * 256 + gt, d_ = slot_ / 16, c_ = slot_ % 16;                    \
-    *reinterpret_cast<uint4*>((BUF) + d_ * VSTR + c_ * 16) = VAR;                          \
+    *reinterpret_cast<u32x4*>((BUF) + d_ * VSTR + c_ * 16) = VAR;                          \
   }
-#define RF_LOAD_K(J)                                                                       \
+// Tile J into the staging registers: K rows (as 16-byte chunks, row-major)
+// or V^T. Chunk m of thread gt is bytes [16 (256 m + gt), +16) of the tile in
+// both cases; rows past the end of K read as zeros (and are masked anyway).
+#define RF_LOAD_TILE(RS, SO, NCH)                                                          \
   do {                                                                                     \
-    int64_t fr0_;                                                                          \
-    int32_t flen_;                                                                         \
-    rf_block_rows(g, (J), &fr0_, &flen_);                                                  \
-    const uint8_t* src_ = kbytes + fr0_ * KROW;                                            \
-    RF_KLD1(st0, 0) RF_KLD1(st1, 1) RF_KLD1(st2, 2) RF_KLD1(st3, 3)                        \
-    RF_KLD1(st4, 4) RF_KLD1(st5, 5) RF_KLD1(st6, 6) RF_KLD1(st7, 7)                        \
+    const __amdgpu_buffer_rsrc_t rs_ = (RS);                                               \
+    const int so_ = (SO), nch_ = (NCH);                                                    \
+    RF_GLD1(st0, 0) RF_GLD1(st1, 1) RF_GLD1(st2, 2) RF_GLD1(st3, 3)                        \
+    RF_GLD1(st4, 4) RF_GLD1(st5, 5) RF_GLD1(st6, 6) RF_GLD1(st7, 7)                        \
   } while (0)
+#define RF_LOAD_K(J) RF_LOAD_TILE(rk, k_tile_off(J), K_CH)
 #define RF_STORE_K(BUF)                                                                    \
   do {                                                                                     \
     RF_KST1(BUF, st0, 0) RF_KST1(BUF, st1, 1) RF_KST1(BUF, st2, 2) RF_KST1(BUF, st3, 3)    \
     RF_KST1(BUF, st4, 4) RF_KST1(BUF, st5, 5) RF_KST1(BUF, st6, 6) RF_KST1(BUF, st7, 7)    \
-  } while (0)
-#define RF_LOAD_V(J)                                                                       \
-  do {                                                                                     \
-    const uint8_t* src_ = vbytes + (int64_t)(J) * D * 256;                                 \
-    RF_VLD1(st0, 0) RF_VLD1(st1, 1) RF_VLD1(st2, 2) RF_VLD1(st3, 3)                        \
-    RF_VLD1(st4, 4) RF_VLD1(st5, 5) RF_VLD1(st6, 6) RF_VLD1(st7, 7)                        \
   } while (0)
 #define RF_STORE_V(BUF)                                                                    \
   do {                                                                                     \
@@ -456,37 +465,26 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     // The next tile's global loads ride along with the products, one after
     // every NMFMA / 8 of them, so that no wave stalls on a burst of loads.
     {
-      int64_t fr0_;
-      int32_t flen_;
-      rf_block_rows(g, jcopy, &fr0_, &flen_);
-      const uint8_t* const ksrc_ = kbytes + fr0_ * KROW;
-      const uint8_t* const vsrc_ = vbytes + (int64_t)jcopy * D * 256;
-#define RF_LD(M)                                                                           \
-  if (kh == 0) {                                                                           \
-    const uint8_t* src_ = vsrc_;                                                           \
-    RF_VLD1(st##M, M)                                                                      \
-  } else {                                                                                 \
-    const uint8_t* src_ = ksrc_;                                                           \
-    RF_KLD1(st##M, M)                                                                      \
-  }
+      const __amdgpu_buffer_rsrc_t rs_ = kh == 0 ? rv : rk;
+      const int so_ = kh == 0 ? jcopy * (D * 256) : k_tile_off(jcopy);
+      const int nch_ = kh == 0 ? V_CH : K_CH;
 #define RF_Q(K) ((K) * PL::NMFMA / 8)
       mfma_steps<D, MIX, 0, RF_Q(1)>(c);
-      RF_LD(0)
+      RF_GLD1(st0, 0)
       mfma_steps<D, MIX, RF_Q(1), RF_Q(2)>(c);
-      RF_LD(1)
+      RF_GLD1(st1, 1)
       mfma_steps<D, MIX, RF_Q(2), RF_Q(3)>(c);
-      RF_LD(2)
+      RF_GLD1(st2, 2)
       mfma_steps<D, MIX, RF_Q(3), RF_Q(4)>(c);
-      RF_LD(3)
+      RF_GLD1(st3, 3)
       mfma_steps<D, MIX, RF_Q(4), RF_Q(5)>(c);
-      RF_LD(4)
+      RF_GLD1(st4, 4)
       mfma_steps<D, MIX, RF_Q(5), RF_Q(6)>(c);
-      RF_LD(5)
+      RF_GLD1(st5, 5)
       mfma_steps<D, MIX, RF_Q(6), RF_Q(7)>(c);
-      RF_LD(6)
+      RF_GLD1(st6, 6)
       mfma_steps<D, MIX, RF_Q(7), RF_Q(8)>(c);
-      RF_LD(7)
-#undef RF_LD
+      RF_GLD1(st7, 7)
 #undef RF_Q
     }
     lds_barrier();
@@ -587,11 +585,10 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
 
 #undef RF_LOAD_K
 #undef RF_STORE_K
-#undef RF_LOAD_V
 #undef RF_STORE_V
-#undef RF_KLD1
+#undef RF_GLD1
+#undef RF_LOAD_TILE
 #undef RF_KST1
-#undef RF_VLD1
 #undef RF_VST1
 
   __syncthreads();  // every wave is done with the tiles
@@ -658,6 +655,10 @@ rf_status rf_launch_sparse_attn(const RfGeom& g, int32_t precision, float scale,
   a.out_p = static_cast<uint16_t*>(out_p);
   const int64_t wgs = (int64_t)g.B * g.N1 * g.n_blocks;
   if (wgs > 0x7fffffff) return RF_ERR_SHAPE;
+  // Tile loads address one (batch, kv head)'s K and V^T through 32-bit buffer
+  // offsets.
+  const int64_t krow = precision == RF_PREC_MIX ? g.D : 2 * g.D;
+  if (g.S * krow > 0x7fffffff || (int64_t)g.n_blocks * g.D * 256 > 0x7fffffff) return RF_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((uint32_t)wgs);
   const bool mix = precision == RF_PREC_MIX;

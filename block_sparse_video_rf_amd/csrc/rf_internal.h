@@ -34,22 +34,17 @@ struct RfGeom {
   int64_t prom_per_frame;      // promoted rows of one paired frame: H*W - (8*tiles_h)*(8*tiles_w)
 };
 
-// Rows of block j: first permuted row and length (1..128).
+// Rows of block j: first permuted row and length (1..128). Head blocks tile
+// [0, HF); every later block (sparse segment, then tail) starts at
+// HF + 128 (j - n_head) and ends at most at S (S = HF + 128 n_sparse + U, so
+// sparse blocks are always whole). Written without branches: kernels call it
+// per listed block.
 RF_HD void rf_block_rows(const RfGeom& g, int32_t j, int64_t* row0, int32_t* len) {
-  if (j < g.n_head) {
-    int64_t r0 = (int64_t)j * 128;
-    int64_t n = g.HF - r0;
-    *row0 = r0;
-    *len = (int32_t)(n < 128 ? n : 128);
-  } else if (j < g.n_head + g.n_sparse) {
-    *row0 = g.HF + (int64_t)(j - g.n_head) * 128;
-    *len = 128;
-  } else {
-    int64_t t0 = (int64_t)(j - g.n_head - g.n_sparse) * 128;
-    int64_t n = g.U - t0;
-    *row0 = g.HF + (int64_t)g.n_sparse * 128 + t0;
-    *len = (int32_t)(n < 128 ? n : 128);
-  }
+  const bool head = j < g.n_head;
+  const int64_t r0 = head ? (int64_t)j * 128 : g.HF + (int64_t)(j - g.n_head) * 128;
+  const int64_t n = (head ? g.HF : g.S) - r0;
+  *row0 = r0;
+  *len = (int32_t)(n < 128 ? n : 128);
 }
 
 // Natural row of the token at permuted row r (0 <= r < S).

@@ -90,7 +90,7 @@ typedef struct rf_desc {
   int32_t heads_q;           /* N1 >= 1 */
   int32_t heads_kv;          /* N2 >= 1, N1 % N2 == 0; query head n uses KV head n / (N1/N2) */
   int32_t head_dim;          /* D: 64 or 128 */
-  int64_t seq_len;           /* S rows per batch item */
+  int64_t seq_len;           /* S rows per batch item; S * head_dim * 2 < 2^31 */
   int32_t block_shape[2];    /* {blockShapeX, blockShapeY} ([ACL]); must be {128, 128} */
   int64_t prefix_len;        /* rows before the video (text, conditions, audio): always dense ([RFA]) */
   int64_t first_frame_rows;  /* 0, or grid_h*grid_w: first latent frame is the dense sink ([RF2]) */

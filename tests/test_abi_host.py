@@ -85,6 +85,7 @@ BAD = [
     ("batch", dict(batch=0), 4),
     ("heads", dict(heads_q=0), 4),
     ("seq", dict(seq_len=0), 4),
+    ("seq_bytes", dict(seq_len=1 << 24), 4),  # 2^24 rows x 64 x 2 B = 2 GiB per head
     ("scale", dict(scale=-1.0), 4),
     ("scale_nan", dict(scale=float("nan")), 4),
     ("block_zero", dict(block_shape=(0, 128)), 5),

@@ -9,8 +9,9 @@ sparsity 0.8, bf16).
 
 Printed (one JSON line): the sparse attention kernel's ms/call (``value``),
 its actual and dense-equivalent TFLOP/s and MFMA-roofline fraction, the
-pipeline ms/step, the same kernel run with every block listed (dense) and the
-speed-up against the ceiling set by the always-dense rows, per-kernel times of
+pipeline ms/step, the same kernel run with every block listed (dense), the
+dense path (rf_dense_attn) and the speed-up against the ceiling set by the
+always-dense rows, per-kernel times of
 the bandwidth-bound steps, and the CPU oracle timed on a bounded sample.
 
 Kernel times come from HIP events recorded on the stream the library
@@ -51,7 +52,46 @@ def parse_args():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure the achievable peaks: a large bf16 GEMM (hipBLASLt) and a "
+                         "device-to-device copy")
     return ap.parse_args()
+
+
+def measure_peaks(torch, dev):
+    """Achievable MFMA and HBM rates on this machine, to read the rooflines against."""
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.mm(a, b, out=c)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        torch.mm(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_ms = e0.elapsed_time(e1) / reps
+    x = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(2):
+        y.copy_(x)
+    e0.record()
+    for _ in range(5):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_ms = e0.elapsed_time(e1) / 5
+    return {"gemm_bf16": {"m": n, "n": n, "k": n, "ms": round(gemm_ms, 4),
+                          "tflops": round(2.0 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+                          "frac_of_published": round(2.0 * n ** 3 / (gemm_ms * 1e-3) / 1e12
+                                                     / PEAK_TFLOPS["bf16"], 3)},
+            "copy": {"bytes_moved": 2 * (1 << 32), "ms": round(copy_ms, 4),
+                     "GB_s": round(2 * (1 << 32) / (copy_ms * 1e-3) / 1e9, 1),
+                     "frac_of_published": round(2 * (1 << 32) / (copy_ms * 1e-3) / 1e9
+                                                / HBM_PEAK_GBS, 3)}}
 
 
 def _block_lengths(info):
@@ -175,6 +215,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.peaks:
+        print(json.dumps({"peaks_measured": measure_peaks(torch, dev)}))
+        return
+
     if args.copy_calibration:
         x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         y = torch.empty_like(x)
@@ -266,9 +310,19 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1) / reps
+        # The dense path proper (rf_dense_attn: same kernel, no lists to read).
+        e0.record(stream)
+        for _ in range(reps):
+            rf.rf_dense_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, out_d,
+                             stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dense_path_ms = e0.elapsed_time(e1) / reps
         dense = {"ms_per_call": round(dense_ms, 3), "speedup": round(dense_ms / attn_ms, 3),
                  "speedup_ceiling": round(ceiling, 3),
-                 "tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 1)}
+                 "tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 1),
+                 "dense_path_ms": round(dense_path_ms, 3),
+                 "dense_path_tflops": round(dense_flops / (dense_path_ms * 1e-3) / 1e12, 1)}
         del idx_d, num_d, out_d
 
     S, D, N1, N2, B = w.seq_len, w.head_dim, w.heads_q, w.heads_kv, w.batch

@@ -3,10 +3,12 @@
 The compute lives in the HIP library ``librf.so`` (C ABI in ``include/rf.h``);
 ``rf`` is its ctypes binding. PyTorch supplies device memory and streams only.
 """
-from .rf import (Buffers, Desc, RfError, RfPlanInfo, attention, load_library, rf_permute,
-                 rf_plan, rf_pool_select, rf_sparse_attn, rf_status_str, rf_unpermute,
-                 rf_version, EXPORTS, LIB_PATH)
+from .rf import (Buffers, Desc, RfError, RfPlanInfo, attention, dense_attention, load_library,
+                 rf_dense_attn, rf_permute, rf_plan, rf_pool_select, rf_sparse_attn,
+                 rf_status_str, rf_unpermute, rf_version, EXPORTS, LIB_PATH)
+from .schedule import DenseSchedule, parse_layers, scheduled_attention
 
-__all__ = ["Buffers", "Desc", "RfError", "RfPlanInfo", "attention", "load_library",
-           "rf_permute", "rf_plan", "rf_pool_select", "rf_sparse_attn", "rf_status_str",
-           "rf_unpermute", "rf_version", "EXPORTS", "LIB_PATH"]
+__all__ = ["Buffers", "DenseSchedule", "Desc", "RfError", "RfPlanInfo", "attention",
+           "dense_attention", "load_library", "parse_layers", "rf_dense_attn", "rf_permute",
+           "rf_plan", "rf_pool_select", "rf_sparse_attn", "rf_status_str", "rf_unpermute",
+           "rf_version", "scheduled_attention", "EXPORTS", "LIB_PATH"]

@@ -219,6 +219,30 @@ rf_status rf_sparse_attn(const rf_desc* desc, const void* qp, const void* kp, co
                                k_scale, select_idx, select_num, max_kv, out_p, stream);
 }
 
+rf_status rf_dense_attn(const rf_desc* desc, const void* qp, const void* kp, const void* vpt,
+                        const uint8_t* q8, const uint8_t* k8, const float* q_scale,
+                        const float* k_scale, void* out_p, void* stream) {
+  RfGeom g;
+  rf_plan_info pi;
+  rf_status s = rf_derive(desc, &g, &pi);
+  if (s != RF_OK) return s;
+  if (!vpt || !out_p) return RF_ERR_NULL;
+  const bool mix = desc->precision == RF_PREC_MIX;
+  if (mix) {
+    if (!q8 || !k8 || !q_scale || !k_scale) return RF_ERR_PRECISION;
+  } else if (!qp || !kp) {
+    return RF_ERR_NULL;
+  }
+  const size_t ob = (size_t)pi.qp_elems * 2;
+  if (overlaps(out_p, ob, qp, ob) || overlaps(out_p, ob, kp, (size_t)pi.kp_elems * 2) ||
+      overlaps(out_p, ob, vpt, (size_t)pi.vpt_elems * 2) ||
+      overlaps(out_p, ob, q8, (size_t)pi.qp_elems) || overlaps(out_p, ob, k8, (size_t)pi.kp_elems))
+    return RF_ERR_ALIAS;
+  // No lists: the kernel walks every block of the head in order.
+  return rf_launch_sparse_attn(g, desc->precision, desc->scale, qp, kp, vpt, q8, k8, q_scale,
+                               k_scale, nullptr, nullptr, g.n_blocks, out_p, stream);
+}
+
 rf_status rf_unpermute(const rf_desc* desc, const void* out_p, void* out, void* stream) {
   RfGeom g;
   rf_plan_info pi;

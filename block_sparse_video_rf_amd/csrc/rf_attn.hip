@@ -273,7 +273,9 @@ __device__ __forceinline__ void mfma_steps(MfmaCtx<D, MIX>& c) {
 // Barriers wait only for LDS operations (lds_barrier), and the block ids come
 // from a window of list entries held in scalar registers, so no wait in the
 // loop covers anything but the data it needs.
-template <int D, bool MIX>
+//
+// ALL (the dense path, no lists) visits every key block in order.
+template <int D, bool MIX, bool ALL>
 __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   using PL = MfmaPlan<D, MIX>;
   constexpr int KROW = MIX ? D : 2 * D;  // K row bytes in global memory
@@ -350,8 +352,8 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int64_t sel_row = ((int64_t)b * g.n_blocks + q) * g.N1 + n;
-  const list_ptr list = (list_ptr)(a.select_idx + sel_row * a.max_kv);
-  int32_t cnt = ((list_ptr)a.select_num)[sel_row];
+  const list_ptr list = ALL ? nullptr : (list_ptr)(a.select_idx + sel_row * a.max_kv);
+  int32_t cnt = ALL ? g.n_blocks : ((list_ptr)a.select_num)[sel_row];
   cnt = cnt < 0 ? 0 : (cnt > a.max_kv ? a.max_kv : cnt);
 
   const uint8_t* kbytes =
@@ -419,7 +421,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   // as skipping it. Entries past the list end stand for block 0 too; nothing
   // reads what is fetched for them.
   const int32_t nbk = g.n_blocks;
-  auto entry = [&](int pos) -> int32_t { return pos < cnt ? list[pos] : -1; };
+  auto entry = [&](int pos) -> int32_t { return pos < cnt ? (ALL ? pos : list[pos]) : -1; };
   auto safe = [&](int32_t jr) -> int32_t { return (jr >= 0 && jr < nbk) ? jr : 0; };
   int32_t w0 = entry(0), w1 = entry(1), w2 = entry(2), w3 = entry(3);
 
@@ -662,16 +664,14 @@ rf_status rf_launch_sparse_attn(const RfGeom& g, int32_t precision, float scale,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((uint32_t)wgs);
   const bool mix = precision == RF_PREC_MIX;
-  if (g.D == 128) {
-    if (mix)
-      hipLaunchKernelGGL((sparse_attn_kernel<128, true>), grid, dim3(kThreads8), 0, s, a);
-    else
-      hipLaunchKernelGGL((sparse_attn_kernel<128, false>), grid, dim3(kThreads8), 0, s, a);
-  } else {
-    if (mix)
-      hipLaunchKernelGGL((sparse_attn_kernel<64, true>), grid, dim3(kThreads8), 0, s, a);
-    else
-      hipLaunchKernelGGL((sparse_attn_kernel<64, false>), grid, dim3(kThreads8), 0, s, a);
-  }
+  const bool all = select_idx == nullptr;
+  // One instantiation per (head_dim, precision, lists or none).
+  using Kern = void (*)(AttnArgs);
+  static const Kern kernels[2][2][2] = {
+      {{sparse_attn_kernel<64, false, false>, sparse_attn_kernel<64, false, true>},
+       {sparse_attn_kernel<64, true, false>, sparse_attn_kernel<64, true, true>}},
+      {{sparse_attn_kernel<128, false, false>, sparse_attn_kernel<128, false, true>},
+       {sparse_attn_kernel<128, true, false>, sparse_attn_kernel<128, true, true>}}};
+  hipLaunchKernelGGL(kernels[g.D == 128][mix][all], grid, dim3(kThreads8), 0, s, a);
   return hipGetLastError() == hipSuccess ? RF_OK : RF_ERR_HIP;
 }

@@ -52,8 +52,8 @@ class RfPlanInfo(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
-EXPORTS = ("rf_plan", "rf_permute", "rf_pool_select", "rf_sparse_attn", "rf_unpermute",
-           "rf_status_str", "rf_version")
+EXPORTS = ("rf_plan", "rf_permute", "rf_pool_select", "rf_sparse_attn", "rf_dense_attn",
+           "rf_unpermute", "rf_status_str", "rf_version")
 
 _lib = None
 
@@ -73,8 +73,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rf_permute.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.rf_pool_select.argtypes = [D, P, P, P, P, P, P, ctypes.c_int32, P, ctypes.c_size_t, P]
     lib.rf_sparse_attn.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, P]
+    lib.rf_dense_attn.argtypes = [D, P, P, P, P, P, P, P, P, P]
     lib.rf_unpermute.argtypes = [D, P, P, P]
-    for f in ("rf_plan", "rf_permute", "rf_pool_select", "rf_sparse_attn", "rf_unpermute"):
+    for f in ("rf_plan", "rf_permute", "rf_pool_select", "rf_sparse_attn", "rf_dense_attn",
+              "rf_unpermute"):
         getattr(lib, f).restype = ctypes.c_int
     lib.rf_status_str.argtypes = [ctypes.c_int]
     lib.rf_status_str.restype = ctypes.c_char_p
@@ -193,6 +195,13 @@ def rf_sparse_attn(desc: Desc, qp, kp, vpt, q8, k8, q_scale, k_scale, select_idx
         _stream(stream)))
 
 
+def rf_dense_attn(desc: Desc, qp, kp, vpt, q8, k8, q_scale, k_scale, out_p, stream=None):
+    d = desc.c()
+    _check("rf_dense_attn", load_library().rf_dense_attn(
+        ctypes.byref(d), _ptr(qp), _ptr(kp), _ptr(vpt), _ptr(q8), _ptr(k8), _ptr(q_scale),
+        _ptr(k_scale), _ptr(out_p), _stream(stream)))
+
+
 def rf_unpermute(desc: Desc, out_p, out, stream=None):
     d = desc.c()
     _check("rf_unpermute", load_library().rf_unpermute(ctypes.byref(d), _ptr(out_p), _ptr(out),
@@ -200,9 +209,13 @@ def rf_unpermute(desc: Desc, out_p, out, stream=None):
 
 
 class Buffers:
-    """Device buffers for one call shape, sized from ``rf_plan`` (torch allocations)."""
+    """Device buffers for one call shape, sized from ``rf_plan`` (torch allocations).
 
-    def __init__(self, desc: Desc, device="cuda"):
+    ``lists=False`` leaves out what only the sparse path uses (pooled blocks,
+    selectIdx / selectNum, the selection workspace): the dense path needs none.
+    """
+
+    def __init__(self, desc: Desc, device="cuda", lists: bool = True):
         import torch
         self.desc = desc
         self.info = info = rf_plan(desc)
@@ -213,16 +226,19 @@ class Buffers:
         self.qp = None if mix else torch.empty((B, N1, S, D), dtype=bf, device=device)
         self.kp = None if mix else torch.empty((B, N2, S, D), dtype=bf, device=device)
         self.vpt = torch.empty((B, N2, nB, D, 128), dtype=bf, device=device)
-        self.q_pool = torch.empty((B, N1, nS, D), dtype=torch.float32, device=device)
-        self.k_pool = torch.empty((B, N2, nS, D), dtype=torch.float32, device=device)
+        f32 = torch.float32
+        self.q_pool = torch.empty((B, N1, nS, D), dtype=f32, device=device) if lists else None
+        self.k_pool = torch.empty((B, N2, nS, D), dtype=f32, device=device) if lists else None
         self.q8 = torch.empty((B, N1, S, D), dtype=torch.uint8, device=device) if mix else None
         self.k8 = torch.empty((B, N2, S, D), dtype=torch.uint8, device=device) if mix else None
         self.q_scale = torch.empty((B, N1, nB), dtype=torch.float32, device=device) if mix else None
         self.k_scale = torch.empty((B, N2, nB), dtype=torch.float32, device=device) if mix else None
-        self.select_idx = torch.empty((B * nB, N1, nB), dtype=torch.int32, device=device)
-        self.select_num = torch.empty((B * nB, N1), dtype=torch.int32, device=device)
-        self.workspace = torch.empty((max(1, info.ws_select_bytes),), dtype=torch.uint8,
-                                     device=device)
+        self.select_idx = (torch.empty((B * nB, N1, nB), dtype=torch.int32, device=device)
+                           if lists else None)
+        self.select_num = (torch.empty((B * nB, N1), dtype=torch.int32, device=device)
+                           if lists else None)
+        self.workspace = (torch.empty((max(1, info.ws_select_bytes),), dtype=torch.uint8,
+                                      device=device) if lists else None)
         self.out_p = torch.empty((B, N1, S, D), dtype=bf, device=device)
 
 
@@ -245,5 +261,27 @@ def attention(q, k, v, desc: Desc, bufs: Optional[Buffers] = None, out=None, str
                    b.workspace, stream=stream)
     rf_sparse_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, b.select_idx,
                    b.select_num, nB, b.out_p, stream=stream)
+    rf_unpermute(desc, b.out_p, out, stream=stream)
+    return out, bufs
+
+
+def dense_attention(q, k, v, desc: Desc, bufs: Optional[Buffers] = None, out=None, stream=None):
+    """The dense path: permute -> attention over every block -> unpermute.
+
+    Same inputs and output as ``attention``; no pooling, no selection, no
+    lists. Full attention is independent of the key order, so the result is
+    full attention in the caller's order (for mix precision: with the same
+    per-block E4M3 Q/K as the sparse path).
+    """
+    import torch
+    if bufs is None:
+        bufs = Buffers(desc, device=q.device, lists=False)
+    if out is None:
+        out = torch.empty_like(q)
+    b = bufs
+    rf_permute(desc, q, k, v, b.qp, b.kp, b.vpt, None, None, b.q8, b.k8, b.q_scale, b.k_scale,
+               stream=stream)
+    rf_dense_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, b.out_p,
+                  stream=stream)
     rf_unpermute(desc, b.out_p, out, stream=stream)
     return out, bufs

@@ -9,6 +9,7 @@
  *                   sparse blocks, and (mix precision) quantise Q/K to fp8
  *   rf_pool_select  score pooled blocks and build selectIdx / selectNum
  *   rf_sparse_attn  exact softmax attention restricted to the listed blocks
+ *   rf_dense_attn   the same attention over every block (the dense path)
  *   rf_unpermute    undo the arrangement
  *
  * Sources (cited by page title and section):
@@ -195,6 +196,20 @@ rf_status rf_sparse_attn(const rf_desc* desc, const void* qp, const void* kp, co
                          const uint8_t* q8, const uint8_t* k8, const float* q_scale,
                          const float* k_scale, const int32_t* select_idx,
                          const int32_t* select_num, int32_t max_kv, void* out_p, void* stream);
+
+/* Dense path. [RFA] introduction: calls that RainFusion does not handle, and
+ * the steps and layers its Configuration keeps dense (start_step, end_step,
+ * skip_layers), delegate to full attention (FLASH_ATTN there).
+ * out = softmax(scale * Q K^T) V over every key row of the sequence, computed
+ * on the same buffers as rf_sparse_attn with every block listed in order. No
+ * list is read, so none needs to be built. Full attention does not depend on
+ * the order of the keys, so any arrangement that rf_permute made gives the
+ * same result (after rf_unpermute) as full attention in the caller's order.
+ * Arguments, layouts and errors as rf_sparse_attn without the lists.
+ * out_p: bf16 [B, N1, S, D], permuted row order, rounded to nearest even. */
+rf_status rf_dense_attn(const rf_desc* desc, const void* qp, const void* kp, const void* vpt,
+                        const uint8_t* q8, const uint8_t* k8, const float* q_scale,
+                        const float* k_scale, void* out_p, void* stream);
 
 /* Step 5. [XPR] commit summary (inverse rearrange; roundtrip check).
  * out[natural row pi(r)] = out_p[r]; out in the caller's layout with heads_q

@@ -122,6 +122,8 @@ def test_invalid_descriptors(name, change, status):
                               1 << 30, None) == status
     assert lib.rf_sparse_attn(ctypes.byref(c), fake, fake, fake, None, None, None, None, fake,
                               fake, 1000, fake, None) == status
+    assert lib.rf_dense_attn(ctypes.byref(c), fake, fake, fake, None, None, None, None, fake,
+                             None) == status
     assert lib.rf_unpermute(ctypes.byref(c), fake, fake, None) == status
 
 

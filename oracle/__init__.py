@@ -31,13 +31,15 @@ quality (it needs trained models and a video benchmark): parity unpinned.
 """
 from .geometry import Geometry, plan, permutation, permute_rows, unpermute_rows, block_rows
 from .select import pool_blocks, block_scores, topk_sparse, select_lists, num_kept
-from .attention import sparse_attention, attention_block
-from .fp8 import e4m3_decode, e4m3_encode, quantize_blocks
+from .attention import sparse_attention, attention_block, attention_block_fp8p
+from .fp8 import (e4m3_decode, e4m3_encode, e4m3_round, quantize_blocks, quantize_blocks_pow2,
+                  pow2_scale_exponent)
 from .pipeline import run
 
 __all__ = [
     "Geometry", "plan", "permutation", "permute_rows", "unpermute_rows", "block_rows",
     "pool_blocks", "block_scores", "topk_sparse", "select_lists", "num_kept",
-    "sparse_attention", "attention_block", "e4m3_decode", "e4m3_encode", "quantize_blocks",
-    "run",
+    "sparse_attention", "attention_block", "attention_block_fp8p", "e4m3_decode",
+    "e4m3_encode", "e4m3_round", "quantize_blocks", "quantize_blocks_pow2",
+    "pow2_scale_exponent", "run",
 ]

@@ -15,11 +15,30 @@ blocks).
 
 Float64 throughout: logits, the row maximum, exponentials, the row sum and
 the weighted sum of V.
+
+"fp8" precision ("RainFusion Attention", Configuration, names it without a
+definition) also quantises the probabilities. Reading, after the
+pre-normalisation idea of MXAttention (catalyzex author page, abstract: the
+unnormalised softmax exponentials are quantised before the row sum, so the
+normalisation holds by construction):
+
+* logits in log2 units ``t_c = scale * <q, k_c> / ln 2``;
+* reference ``M = ceil(max_c t_c)``, the row maximum rounded up to an
+  integer, so the largest exponential lies in (1/2, 1] and the reference is a
+  power of two;
+* ``P_c = e4m3(2**(t_c - M))`` (nearest, ties to even);
+* ``O = sum_c P_c v_c / sum_c P_c`` - the row sum is the sum of the quantised
+  values that multiply V.
+
+A power-of-two reference makes the codes independent of which power of two a
+streaming kernel happens to hold as its running reference (scaling by 2**k
+commutes with E4M3 rounding of normal values).
 """
 from __future__ import annotations
 
 import numpy as np
 
+from .fp8 import e4m3_round
 from .geometry import Plan
 
 
@@ -34,6 +53,19 @@ def attention_block(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -
     return (e @ np.asarray(v, dtype=np.float64)) / e.sum(axis=1, keepdims=True)
 
 
+def attention_block_fp8p(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """Attention with E4M3 probabilities quantised before the row sum (float64).
+
+    ``q [M, D]`` against ``k, v [L, D]`` (already dequantised operands)."""
+    q = np.asarray(q, dtype=np.float64)
+    if k.shape[0] == 0:
+        return np.zeros((q.shape[0], v.shape[1]), dtype=np.float64)
+    t = (scale / np.log(2.0)) * (q @ np.asarray(k, dtype=np.float64).T)
+    ref = np.ceil(t.max(axis=1, keepdims=True))
+    pq = e4m3_round(np.exp2(t - ref))
+    return (pq @ np.asarray(v, dtype=np.float64)) / pq.sum(axis=1, keepdims=True)
+
+
 def listed_rows(p: Plan, ids) -> np.ndarray:
     """Permuted row indices covered by the listed block ids, in list order."""
     parts = [np.arange(p.blocks[j][0], p.blocks[j][0] + p.blocks[j][1]) for j in ids]
@@ -41,13 +73,15 @@ def listed_rows(p: Plan, ids) -> np.ndarray:
 
 
 def sparse_attention(qp, kp, vp, p: Plan, select_idx, select_num, scale: float,
-                     query_blocks=None) -> np.ndarray:
+                     query_blocks=None, quantize_p: bool = False) -> np.ndarray:
     """Permuted-order attention output ``[B, N1, S, D]`` (float64).
 
     ``qp``: ``[B, N1, S, D]``; ``kp``, ``vp``: ``[B, N2, S, D]`` (permuted rows,
     any real dtype). ``query_blocks``: optional iterable of ``(b, q, n)`` to
     evaluate only those (query block, head) pairs; other rows stay zero.
+    ``quantize_p``: E4M3 probabilities ("fp8" precision, ``attention_block_fp8p``).
     """
+    block = attention_block_fp8p if quantize_p else attention_block
     B, N1, S, D = qp.shape
     G = N1 // kp.shape[1]
     nB = p.n_blocks
@@ -59,6 +93,6 @@ def sparse_attention(qp, kp, vp, p: Plan, select_idx, select_num, scale: float,
         row = b * nB + q
         ids = select_idx[row, n, :select_num[row, n]]
         rows = listed_rows(p, ids)
-        out[b, n, r0:r0 + m] = attention_block(qp[b, n, r0:r0 + m], kp[b, n // G, rows],
-                                               vp[b, n // G, rows], scale)
+        out[b, n, r0:r0 + m] = block(qp[b, n, r0:r0 + m], kp[b, n // G, rows],
+                                     vp[b, n // G, rows], scale)
     return out

@@ -1,4 +1,4 @@
-"""OCP FP8 E4M3 codec and the per-block quantisation of the "mix" precision.
+"""OCP FP8 E4M3 codec and the per-block quantisation of the "mix" and "fp8" precisions.
 
 TEST INFRASTRUCTURE (see the package docstring).
 
@@ -25,6 +25,19 @@ fixed here and the GPU path does the same float32 operations):
 * an all-zero block uses ``r = sigma = 1``.
 
 The dequantised value is ``decode(code) * sigma``.
+
+The "fp8" precision (same Configuration row, equally undefined there) is read
+as every attention operand in E4M3: Q and K exactly as in "mix"; V per
+(batch, kv head, 128-row block) with a power-of-two scale (below); and the
+probabilities P as E4M3 codes of the unnormalised exponentials (``attention.py``).
+
+Power-of-two block scale (V in "fp8"): ``sigma = 2**e`` with ``e`` the
+smallest integer such that ``amax <= 448 * 2**e``, clamped to [-126, 127]
+(so sigma is a normal float32); an all-zero block uses ``e = 0``. Then
+``code = e4m3(x / sigma)``: dividing by a power of two is exact, so the codes
+depend on the values alone, and the block's largest magnitude lands in
+(224, 448]. A power-of-two scale is what the gfx950 scaled fp8 products take
+as a per-operand block exponent (E8M0), so the kernel applies it exactly.
 """
 from __future__ import annotations
 
@@ -92,3 +105,40 @@ def quantize_blocks(xp_f32: np.ndarray, p: Plan):
         codes[:, :, r0:r0 + n, :] = e4m3_encode(y)
         sigma[:, :, j] = sig
     return codes, sigma
+
+
+POW2_EXP_MIN, POW2_EXP_MAX = -126, 127
+
+
+def pow2_scale_exponent(amax) -> np.ndarray:
+    """Smallest integer ``e`` with ``amax <= 448 * 2**e`` (clamped to [-126, 127]);
+    0 where ``amax == 0``. The estimate from log2 is corrected by exact float64
+    comparisons (``448 * 2**e`` is exact), so the result is exact."""
+    a = np.asarray(amax, dtype=np.float64)
+    pos = a > 0
+    e = np.ceil(np.log2(np.where(pos, a, E4M3_MAX) / E4M3_MAX))
+    e = np.where(E4M3_MAX * np.exp2(e) < a, e + 1, e)           # too small: step up
+    e = np.where(E4M3_MAX * np.exp2(e - 1) >= a, e - 1, e)      # not the smallest: step down
+    e = np.where(pos, e, 0)
+    return np.clip(e, POW2_EXP_MIN, POW2_EXP_MAX).astype(np.int64)
+
+
+def quantize_blocks_pow2(xp_f32: np.ndarray, p: Plan):
+    """Quantise permuted ``[B, N, S, D]`` values per (batch, head, block) with a
+    power-of-two scale. Returns ``(codes uint8 [B, N, S, D], sigma float32 [B, N, n_blocks])``."""
+    x = np.asarray(xp_f32, dtype=np.float64)
+    B, N, S, D = x.shape
+    codes = np.zeros((B, N, S, D), dtype=np.uint8)
+    sigma = np.ones((B, N, p.n_blocks), dtype=np.float32)
+    for j, (r0, n) in enumerate(p.blocks):
+        blk = x[:, :, r0:r0 + n, :]
+        amax = np.abs(blk).max(axis=(2, 3))                              # [B, N]
+        sig = np.exp2(pow2_scale_exponent(amax).astype(np.float64))     # [B, N]
+        codes[:, :, r0:r0 + n, :] = e4m3_encode(blk / sig[:, :, None, None])
+        sigma[:, :, j] = sig.astype(np.float32)
+    return codes, sigma
+
+
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """Values rounded to E4M3 (nearest, ties to even, saturating): decode(encode(x))."""
+    return e4m3_decode(e4m3_encode(x))

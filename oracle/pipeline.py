@@ -6,8 +6,10 @@ TEST INFRASTRUCTURE (see the package docstring).
 2. pool the sparse blocks of Q and K (``select.py``);
 3. score and keep the top-k key blocks per sparse query block (``select.py``);
 4. exact softmax attention over the listed blocks (``attention.py``),
-   with Q/K replaced by their fp8 E4M3 dequantised values in "mix" precision
-   (``fp8.py``); selection always uses the unquantised Q/K;
+   with Q/K replaced by their fp8 E4M3 dequantised values in "mix" and "fp8"
+   precision, V by its power-of-two-scaled E4M3 values and P by E4M3
+   exponentials in "fp8" (``fp8.py``, ``attention.py``); selection always uses
+   the unquantised Q/K;
 5. undo the arrangement.
 """
 from __future__ import annotations
@@ -17,7 +19,7 @@ import math
 import numpy as np
 
 from .attention import sparse_attention
-from .fp8 import e4m3_decode, quantize_blocks
+from .fp8 import e4m3_decode, quantize_blocks, quantize_blocks_pow2
 from .geometry import Geometry, permutation, permute_rows, plan, unpermute_rows
 from .select import block_scores, pool_blocks, select_lists
 
@@ -66,16 +68,21 @@ def run(q, k, v, g: Geometry, scale: float | None = None, precision: str = "bf16
     res["select_idx"], res["select_num"] = sel
     if select is not None:
         sel = select
-    q_att, k_att = qp, kp
-    if precision == "mix":
+    q_att, k_att, v_att = qp, kp, vp
+    if precision in ("mix", "fp8"):
         q8, sq = quantize_blocks(qp, p)
         k8, sk = quantize_blocks(kp, p)
         res.update(q8=q8, k8=k8, q_scale=sq, k_scale=sk)
         q_att = e4m3_decode(q8) * _expand_block_scale(sq, p, S)
         k_att = e4m3_decode(k8) * _expand_block_scale(sk, p, S)
+        if precision == "fp8":
+            v8, sv = quantize_blocks_pow2(vp, p)
+            res.update(v8=v8, v_scale=sv)
+            v_att = e4m3_decode(v8) * _expand_block_scale(sv, p, S)
     elif precision != "bf16":
-        raise ValueError(f"precision must be bf16 or mix, got {precision!r}")
-    out_p = sparse_attention(q_att, k_att, vp, p, sel[0], sel[1], scale, query_blocks)
+        raise ValueError(f"precision must be bf16, mix or fp8, got {precision!r}")
+    out_p = sparse_attention(q_att, k_att, v_att, p, sel[0], sel[1], scale, query_blocks,
+                             quantize_p=precision == "fp8")
     res["out_p"] = out_p
     out = unpermute_rows(out_p, pi)
     if layout == "TND":

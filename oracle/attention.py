@@ -23,16 +23,18 @@ unnormalised softmax exponentials are quantised before the row sum, so the
 normalisation holds by construction):
 
 * logits in log2 units ``t_c = scale * <q, k_c> / ln 2``;
-* reference ``M = ceil(max_c t_c)``, the row maximum rounded up to an
-  integer, so the largest exponential lies in (1/2, 1] and the reference is a
-  power of two;
-* ``P_c = e4m3(2**(t_c - M))`` (nearest, ties to even);
+* reference ``M = ceil(max_c t_c)``, the row maximum rounded up to an integer;
+* ``P_c = e4m3(2**(t_c - M + 8))`` (nearest, ties to even): the exponentials
+  scaled by a power of two so that the largest lies in (128, 256], the top
+  binades of E4M3 (largest finite 448) - the same use of the full E4M3 range
+  as the block scales of Q, K and V;
 * ``O = sum_c P_c v_c / sum_c P_c`` - the row sum is the sum of the quantised
   values that multiply V.
 
-A power-of-two reference makes the codes independent of which power of two a
-streaming kernel happens to hold as its running reference (scaling by 2**k
-commutes with E4M3 rounding of normal values).
+Scaling by 2**k commutes with E4M3 rounding of normal values, so a one-pass
+kernel that holds a smaller integer reference for earlier blocks rounds them
+the same way; only values below 2**-6 (subnormal, below 2**-14 of the largest
+P) can round differently, and their weight is negligible.
 """
 from __future__ import annotations
 
@@ -62,7 +64,7 @@ def attention_block_fp8p(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: flo
         return np.zeros((q.shape[0], v.shape[1]), dtype=np.float64)
     t = (scale / np.log(2.0)) * (q @ np.asarray(k, dtype=np.float64).T)
     ref = np.ceil(t.max(axis=1, keepdims=True))
-    pq = e4m3_round(np.exp2(t - ref))
+    pq = e4m3_round(np.exp2(t - ref + 8.0))
     return (pq @ np.asarray(v, dtype=np.float64)) / pq.sum(axis=1, keepdims=True)
 
 

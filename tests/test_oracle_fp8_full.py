@@ -109,7 +109,7 @@ def _fp8p_by_loops(q, k, v, scale):
     for qi in q:
         t = [scale / math.log(2.0) * sum(a * b for a, b in zip(qi, kc)) for kc in k]
         ref = math.ceil(max(t))
-        pq = [_nearest_code_value(2.0 ** (tc - ref)) for tc in t]
+        pq = [_nearest_code_value(2.0 ** (tc - ref + 8)) for tc in t]
         den = sum(pq)
         out.append([sum(pq[c] * v[c][d] for c in range(len(k))) / den for d in range(len(v[0]))])
     return np.array(out)
@@ -133,30 +133,37 @@ def _two_keys(t0, t1, v):
 
 def test_fp8p_closed_forms():
     v = np.array([[1.0, -2.0], [5.0, 7.0]])
-    # Equal logits: every P is 1, the output is the mean.
+    # Equal logits: every P is 256, the output is the mean.
     np.testing.assert_allclose(
         attention_block_fp8p(np.zeros((1, 3)), np.ones((4, 3)), np.arange(8.0).reshape(4, 2), 1.0),
         [[3.0, 4.0]], atol=1e-15)
     # Integer logits: exact powers of two.
     np.testing.assert_allclose(_two_keys(3.0, 2.0, v), (v[0] + 0.5 * v[1]) / 1.5, atol=1e-15)
-    # 0.95 rounds to 0.9375, and the row sum is the sum of the rounded values.
+    # 256 * 0.95 = 243.2 rounds to 240 (step 16 in [128, 256)), and the row sum is
+    # the sum of the rounded values: 256 and 240.
     np.testing.assert_allclose(_two_keys(0.0, math.log2(0.95), v),
-                               (v[0] + 0.9375 * v[1]) / 1.9375, atol=1e-15)
-    # The reference is ceil(max) = 3, not the maximum 2.3: P = (0.625, 0.125).
+                               (256 * v[0] + 240 * v[1]) / 496, atol=1e-15)
+    # The reference is ceil(max) = 3, not the maximum 2.3: P = (2^7.3, 2^5) rounds
+    # to (160, 32); with the maximum as reference it would be (256, 52).
     np.testing.assert_allclose(_two_keys(2.3, 0.0, v), (5 * v[0] + v[1]) / 6, atol=1e-15)
-    # Subnormal exponentials: 2^-8 is exact, 2^-9.5 rounds to 2^-9, 2^-11 to 0.
-    np.testing.assert_allclose(_two_keys(0.0, -8.0, v), (v[0] + 2.0 ** -8 * v[1]) / (1 + 2.0 ** -8),
-                               atol=1e-15)
-    np.testing.assert_allclose(_two_keys(0.0, -9.5, v), (v[0] + 2.0 ** -9 * v[1]) / (1 + 2.0 ** -9),
-                               atol=1e-15)
-    np.testing.assert_allclose(_two_keys(0.0, -11.0, v), v[0], atol=0)
+    # With the largest P at 2^8, a key 9.5 below it gets 2^-1.5 = 0.354, a normal
+    # value that rounds to 11/32; with the largest P at 1 it would be subnormal
+    # and round to 2^-9.
+    np.testing.assert_allclose(_two_keys(0.0, -9.5, v),
+                               (256 * v[0] + (11 / 32) * v[1]) / (256 + 11 / 32), atol=1e-15)
+    # Subnormal P (below 2^-6): 2^-7 is exact, 2^-9.5 rounds to 2^-9, 2^-11 to 0.
+    np.testing.assert_allclose(_two_keys(0.0, -15.0, v),
+                               (256 * v[0] + 2.0 ** -7 * v[1]) / (256 + 2.0 ** -7), atol=1e-15)
+    np.testing.assert_allclose(_two_keys(0.0, -17.5, v),
+                               (256 * v[0] + 2.0 ** -9 * v[1]) / (256 + 2.0 ** -9), atol=1e-15)
+    np.testing.assert_allclose(_two_keys(0.0, -19.0, v), v[0], atol=0)
     # No keys: zeros.
     assert np.all(attention_block_fp8p(np.ones((2, 3)), np.zeros((0, 3)), np.zeros((0, 4)), 1.0) == 0)
 
 
 def test_fp8p_within_rounding_bound_of_exact_softmax():
     # |O_q - O| = |sum (P~ - P)(v - O)| / sum P~ <= max|v - O| * sum max(2^-4 P, 2^-10) / sum P~
-    # with P = 2^(t - ceil(max t)) and half an E4M3 quantum per element.
+    # with P = 2^(t - ceil(max t) + 8) and half an E4M3 quantum per element.
     rng = np.random.default_rng(8)
     q = rng.standard_normal((16, 32))
     k = rng.standard_normal((300, 32))
@@ -165,7 +172,7 @@ def test_fp8p_within_rounding_bound_of_exact_softmax():
     exact = attention_block(q, k, v, scale)
     quant = attention_block_fp8p(q, k, v, scale)
     t = scale / math.log(2.0) * (q @ k.T)
-    pe = np.exp2(t - np.ceil(t.max(axis=1, keepdims=True)))
+    pe = np.exp2(t - np.ceil(t.max(axis=1, keepdims=True)) + 8)
     pq = e4m3_round(pe)
     assert np.all(np.abs(pq - pe) <= np.maximum(pe * 2.0 ** -4, 2.0 ** -10))
     spread = np.abs(v[None, :, :] - exact[:, None, :]).max(axis=1)        # [16, 8]

@@ -246,14 +246,14 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         rf.rf_permute(desc, q, k, v, b.qp, b.kp, b.vpt, b.q_pool, b.k_pool, b.q8, b.k8,
-                      b.q_scale, b.k_scale, stream=stream)
+                      b.q_scale, b.k_scale, b.v_scale, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         rf.rf_pool_select(desc, b.qp, b.kp, b.q_pool, b.k_pool, b.select_idx, b.select_num, nB,
                           b.workspace, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        rf.rf_sparse_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale,
+        rf.rf_sparse_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, b.v_scale,
                           b.select_idx, b.select_num, nB, b.out_p, stream=stream)
         if ev is not None:
             ev[3].record(stream)
@@ -289,6 +289,8 @@ def main():
     peak = PEAK_TFLOPS["bf16"]
     if w.precision == "mix":
         peak = 2.0 / (1.0 / PEAK_TFLOPS["fp8"] + 1.0 / PEAK_TFLOPS["bf16"])  # QK^T fp8, PV bf16
+    elif w.precision == "fp8":
+        peak = PEAK_TFLOPS["fp8"]                                            # both products fp8
     ceiling = dense_flops / flops
 
     dense = None
@@ -299,22 +301,22 @@ def main():
         out_d = torch.empty_like(bufs.out_p)
         b = bufs
         for _ in range(2):
-            rf.rf_sparse_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, idx_d,
-                              num_d, nB, out_d, stream=stream)
+            rf.rf_sparse_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale,
+                              b.v_scale, idx_d, num_d, nB, out_d, stream=stream)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         reps = max(3, args.steps // 4)
         e0.record(stream)
         for _ in range(reps):
-            rf.rf_sparse_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, idx_d,
-                              num_d, nB, out_d, stream=stream)
+            rf.rf_sparse_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale,
+                              b.v_scale, idx_d, num_d, nB, out_d, stream=stream)
         e1.record(stream)
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1) / reps
         # The dense path proper (rf_dense_attn: same kernel, no lists to read).
         e0.record(stream)
         for _ in range(reps):
-            rf.rf_dense_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, out_d,
-                             stream=stream)
+            rf.rf_dense_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale,
+                             b.v_scale, out_d, stream=stream)
         e1.record(stream)
         torch.cuda.synchronize()
         dense_path_ms = e0.elapsed_time(e1) / reps
@@ -326,11 +328,13 @@ def main():
         del idx_d, num_d, out_d
 
     S, D, N1, N2, B = w.seq_len, w.head_dim, w.heads_q, w.heads_kv, w.batch
-    # permute: read Q, K, V once; write the permuted Q/K (bf16, or E4M3 codes in mix),
-    # the block-transposed V (blocks padded to 128 columns) and the pooled means.
-    qk_out = 1 if w.precision == "mix" else 2
+    # permute: read Q, K, V once; write the permuted Q/K (bf16, or E4M3 codes in mix
+    # and fp8), the block-transposed V (blocks padded to 128 columns; E4M3 in fp8)
+    # and the pooled means.
+    qk_out = 2 if w.precision == "bf16" else 1
+    v_out = 1 if w.precision == "fp8" else 2
     perm_bytes = (2.0 * S * D * B * (N1 + 2 * N2) + qk_out * S * D * B * (N1 + N2)
-                  + 2.0 * nB * 128 * D * B * N2 + 4.0 * info.n_sparse * D * B * (N1 + N2))
+                  + v_out * nB * 128 * D * B * N2 + 4.0 * info.n_sparse * D * B * (N1 + N2))
     unperm_bytes = 4.0 * S * D * B * N1
     hbm = {
         "permute": {"ms": round(permute_ms, 4), "bytes": perm_bytes,
@@ -352,7 +356,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.precision == "bf16" else "fp8e4m3-qk/bf16-pv",
+        "dtype": {"bf16": "bf16", "mix": "fp8e4m3-qk/bf16-pv", "fp8": "fp8e4m3"}[w.precision],
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads_q": N1, "heads_kv": N2, "head_dim": D,
                    "seq_len": S, "prefix_len": w.prefix_len, "grid": list(w.grid),

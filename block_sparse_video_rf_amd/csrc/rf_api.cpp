@@ -41,8 +41,8 @@ rf_status rf_derive(const rf_desc* d, RfGeom* g, rf_plan_info* info) {
   if (d->heads_q % d->heads_kv != 0) return RF_ERR_GQA;
   if (!isfinite(d->sparsity) || d->sparsity < 0.0 || d->sparsity > 1.0) return RF_ERR_SPARSITY;
   if (!isfinite(d->scale) || !(d->scale > 0.0f)) return RF_ERR_SHAPE;
-  if (d->precision == RF_PREC_FP8) return RF_ERR_UNSUPPORTED;
-  if (d->precision != RF_PREC_BF16 && d->precision != RF_PREC_MIX) return RF_ERR_PRECISION;
+  if (d->precision != RF_PREC_BF16 && d->precision != RF_PREC_MIX && d->precision != RF_PREC_FP8)
+    return RF_ERR_PRECISION;
   // Per-(batch, head) row offsets are formed in 64-bit; keep counts in 32-bit ranges.
   if (d->seq_len > ((int64_t)1 << 31) - 128) return RF_ERR_SHAPE;
   // The attention kernel addresses one (batch, kv head)'s K and V^T with
@@ -127,6 +127,7 @@ rf_status rf_derive(const rf_desc* d, RfGeom* g, rf_plan_info* info) {
     info->k_pool_elems = (int64_t)r.B * r.N2 * r.n_sparse * r.D;
     info->q_scale_elems = (int64_t)r.B * r.N1 * r.n_blocks;
     info->k_scale_elems = (int64_t)r.B * r.N2 * r.n_blocks;
+    info->v_scale_elems = (int64_t)r.B * r.N2 * r.n_blocks;
     info->ws_select_bytes =
         r.fallback ? 0 : rf_ws_scores_bytes(r) + rf_ws_qpool_bytes(r) + rf_ws_kpool_bytes(r);
   }
@@ -142,34 +143,37 @@ rf_status rf_plan(const rf_desc* desc, rf_plan_info* info) {
 
 rf_status rf_permute(const rf_desc* desc, const void* q, const void* k, const void* v, void* qp,
                      void* kp, void* vpt, float* q_pool, float* k_pool, uint8_t* q8, uint8_t* k8,
-                     float* q_scale, float* k_scale, void* stream) {
+                     float* q_scale, float* k_scale, float* v_scale, void* stream) {
   RfGeom g;
   rf_plan_info pi;
   rf_status s = rf_derive(desc, &g, &pi);
   if (s != RF_OK) return s;
-  const bool mix = desc->precision == RF_PREC_MIX;
+  const bool qk8 = desc->precision != RF_PREC_BF16;  // mix and fp8: E4M3 Q/K
+  const bool v8 = desc->precision == RF_PREC_FP8;    // fp8: E4M3 V
   // Each given input needs somewhere to go.
-  if (q && !qp && !q_pool && !(mix && q8)) return RF_ERR_NULL;
-  if (k && !kp && !k_pool && !(mix && k8)) return RF_ERR_NULL;
+  if (q && !qp && !q_pool && !(qk8 && q8)) return RF_ERR_NULL;
+  if (k && !kp && !k_pool && !(qk8 && k8)) return RF_ERR_NULL;
   if (v && !vpt) return RF_ERR_NULL;
-  if (mix && ((q && (!q8 || !q_scale)) || (k && (!k8 || !k_scale)))) return RF_ERR_PRECISION;
+  if (qk8 && ((q && (!q8 || !q_scale)) || (k && (!k8 || !k_scale)))) return RF_ERR_PRECISION;
+  if (v8 && v && !v_scale) return RF_ERR_PRECISION;
   const size_t qb = (size_t)pi.qp_elems * 2, kb = (size_t)pi.kp_elems * 2;
   const size_t vb = kb;
   const void* ins[3] = {q, k, v};
   const size_t insz[3] = {qb, kb, vb};
-  const void* outs[8] = {qp, kp, vpt, q_pool, k_pool, q8, k8, q_scale};
-  const size_t outsz[8] = {qb, kb, (size_t)pi.vpt_elems * 2, (size_t)pi.q_pool_elems * 4,
-                           (size_t)pi.k_pool_elems * 4, (size_t)pi.qp_elems,
-                           (size_t)pi.kp_elems, (size_t)pi.q_scale_elems * 4};
+  const void* outs[10] = {qp, kp, vpt, q_pool, k_pool, q8, k8, q_scale, k_scale, v_scale};
+  const size_t outsz[10] = {qb, kb, (size_t)pi.vpt_elems * (v8 ? 1 : 2),
+                            (size_t)pi.q_pool_elems * 4, (size_t)pi.k_pool_elems * 4,
+                            (size_t)pi.qp_elems, (size_t)pi.kp_elems,
+                            (size_t)pi.q_scale_elems * 4, (size_t)pi.k_scale_elems * 4,
+                            (size_t)pi.v_scale_elems * 4};
   for (int i = 0; i < 3; ++i)
-    for (int o = 0; o < 8; ++o)
+    for (int o = 0; o < 10; ++o)
       if (overlaps(ins[i], insz[i], outs[o], outsz[o])) return RF_ERR_ALIAS;
-  for (int i = 0; i < 3; ++i)
-    if (overlaps(ins[i], insz[i], k_scale, (size_t)pi.k_scale_elems * 4)) return RF_ERR_ALIAS;
   if (!q && !k && !v) return RF_OK;
   return rf_launch_permute(g, desc->precision, q, k, v, qp, kp, vpt, g.fallback ? nullptr : q_pool,
-                           g.fallback ? nullptr : k_pool, mix ? q8 : nullptr, mix ? k8 : nullptr,
-                           mix ? q_scale : nullptr, mix ? k_scale : nullptr, stream);
+                           g.fallback ? nullptr : k_pool, qk8 ? q8 : nullptr, qk8 ? k8 : nullptr,
+                           qk8 ? q_scale : nullptr, qk8 ? k_scale : nullptr,
+                           v8 ? v_scale : nullptr, stream);
 }
 
 rf_status rf_pool_select(const rf_desc* desc, const void* qp, const void* kp, const float* q_pool,
@@ -193,54 +197,66 @@ rf_status rf_pool_select(const rf_desc* desc, const void* qp, const void* kp, co
                                max_kv, workspace, stream);
 }
 
+// Operand checks shared by the two attention entry points: the buffers the
+// precision reads are present, and the output overlaps none of them.
+static rf_status attn_operands(const rf_desc* desc, const RfGeom& g, const rf_plan_info& pi,
+                               const void* qp, const void* kp, const void* vpt, const uint8_t* q8,
+                               const uint8_t* k8, const float* q_scale, const float* k_scale,
+                               const float* v_scale, const void* out_p) {
+  if (!vpt || !out_p) return RF_ERR_NULL;
+  const bool qk8 = desc->precision != RF_PREC_BF16;
+  const bool v8 = desc->precision == RF_PREC_FP8;
+  if (qk8) {
+    if (!q8 || !k8 || !q_scale || !k_scale) return RF_ERR_PRECISION;
+    if (v8 && !v_scale) return RF_ERR_PRECISION;
+  } else if (!qp || !kp) {
+    return RF_ERR_NULL;
+  }
+  const size_t ob = (size_t)pi.qp_elems * 2;
+  if ((!qk8 && (overlaps(out_p, ob, qp, ob) || overlaps(out_p, ob, kp, (size_t)pi.kp_elems * 2))) ||
+      overlaps(out_p, ob, vpt, (size_t)pi.vpt_elems * (v8 ? 1 : 2)) ||
+      (qk8 && (overlaps(out_p, ob, q8, (size_t)pi.qp_elems) ||
+               overlaps(out_p, ob, k8, (size_t)pi.kp_elems) ||
+               overlaps(out_p, ob, q_scale, (size_t)pi.q_scale_elems * 4) ||
+               overlaps(out_p, ob, k_scale, (size_t)pi.k_scale_elems * 4))) ||
+      (v8 && overlaps(out_p, ob, v_scale, (size_t)pi.v_scale_elems * 4)))
+    return RF_ERR_ALIAS;
+  (void)g;
+  return RF_OK;
+}
+
 rf_status rf_sparse_attn(const rf_desc* desc, const void* qp, const void* kp, const void* vpt,
                          const uint8_t* q8, const uint8_t* k8, const float* q_scale,
-                         const float* k_scale, const int32_t* select_idx,
+                         const float* k_scale, const float* v_scale, const int32_t* select_idx,
                          const int32_t* select_num, int32_t max_kv, void* out_p, void* stream) {
   RfGeom g;
   rf_plan_info pi;
   rf_status s = rf_derive(desc, &g, &pi);
   if (s != RF_OK) return s;
-  if (!vpt || !select_idx || !select_num || !out_p) return RF_ERR_NULL;
+  if (!select_idx || !select_num) return RF_ERR_NULL;
   if (max_kv < 1) return RF_ERR_SHAPE;
-  const bool mix = desc->precision == RF_PREC_MIX;
-  if (mix) {
-    if (!q8 || !k8 || !q_scale || !k_scale) return RF_ERR_PRECISION;
-  } else if (!qp || !kp) {
-    return RF_ERR_NULL;
-  }
+  s = attn_operands(desc, g, pi, qp, kp, vpt, q8, k8, q_scale, k_scale, v_scale, out_p);
+  if (s != RF_OK) return s;
   const size_t ob = (size_t)pi.qp_elems * 2;
-  if (overlaps(out_p, ob, qp, ob) || overlaps(out_p, ob, kp, (size_t)pi.kp_elems * 2) ||
-      overlaps(out_p, ob, vpt, (size_t)pi.vpt_elems * 2) ||
-      overlaps(out_p, ob, select_idx, (size_t)pi.select_rows * g.N1 * (size_t)max_kv * 4) ||
-      overlaps(out_p, ob, q8, (size_t)pi.qp_elems) || overlaps(out_p, ob, k8, (size_t)pi.kp_elems))
+  if (overlaps(out_p, ob, select_idx, (size_t)pi.select_rows * g.N1 * (size_t)max_kv * 4) ||
+      overlaps(out_p, ob, select_num, (size_t)pi.select_rows * g.N1 * 4))
     return RF_ERR_ALIAS;
   return rf_launch_sparse_attn(g, desc->precision, desc->scale, qp, kp, vpt, q8, k8, q_scale,
-                               k_scale, select_idx, select_num, max_kv, out_p, stream);
+                               k_scale, v_scale, select_idx, select_num, max_kv, out_p, stream);
 }
 
 rf_status rf_dense_attn(const rf_desc* desc, const void* qp, const void* kp, const void* vpt,
                         const uint8_t* q8, const uint8_t* k8, const float* q_scale,
-                        const float* k_scale, void* out_p, void* stream) {
+                        const float* k_scale, const float* v_scale, void* out_p, void* stream) {
   RfGeom g;
   rf_plan_info pi;
   rf_status s = rf_derive(desc, &g, &pi);
   if (s != RF_OK) return s;
-  if (!vpt || !out_p) return RF_ERR_NULL;
-  const bool mix = desc->precision == RF_PREC_MIX;
-  if (mix) {
-    if (!q8 || !k8 || !q_scale || !k_scale) return RF_ERR_PRECISION;
-  } else if (!qp || !kp) {
-    return RF_ERR_NULL;
-  }
-  const size_t ob = (size_t)pi.qp_elems * 2;
-  if (overlaps(out_p, ob, qp, ob) || overlaps(out_p, ob, kp, (size_t)pi.kp_elems * 2) ||
-      overlaps(out_p, ob, vpt, (size_t)pi.vpt_elems * 2) ||
-      overlaps(out_p, ob, q8, (size_t)pi.qp_elems) || overlaps(out_p, ob, k8, (size_t)pi.kp_elems))
-    return RF_ERR_ALIAS;
+  s = attn_operands(desc, g, pi, qp, kp, vpt, q8, k8, q_scale, k_scale, v_scale, out_p);
+  if (s != RF_OK) return s;
   // No lists: the kernel walks every block of the head in order.
   return rf_launch_sparse_attn(g, desc->precision, desc->scale, qp, kp, vpt, q8, k8, q_scale,
-                               k_scale, nullptr, nullptr, g.n_blocks, out_p, stream);
+                               k_scale, v_scale, nullptr, nullptr, g.n_blocks, out_p, stream);
 }
 
 rf_status rf_unpermute(const rf_desc* desc, const void* out_p, void* out, void* stream) {
@@ -266,7 +282,7 @@ const char* rf_status_str(rf_status status) {
     case RF_ERR_GEOMETRY: return "video grid, prefix or first-frame rows inconsistent with seq_len";
     case RF_ERR_WORKSPACE: return "workspace smaller than rf_plan requires";
     case RF_ERR_UNSUPPORTED: return "valid but not supported by this build (block shape 128x128, "
-                                    "head_dim 64/128, precision bf16/mix, <= 8192 sparse blocks)";
+                                    "head_dim 64/128, <= 8192 sparse blocks)";
     case RF_ERR_PRECISION: return "unknown precision, or a buffer that precision needs is NULL";
     case RF_ERR_HIP: return "HIP launch failed";
     case RF_ERR_ALIAS: return "an output buffer overlaps an input buffer";

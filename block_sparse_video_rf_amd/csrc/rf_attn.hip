@@ -57,6 +57,7 @@ struct AttnArgs {
   const uint8_t* k8;
   const float* q_scale;
   const float* k_scale;
+  const float* v_scale;
   const int32_t* select_idx;
   const int32_t* select_num;
   int32_t max_kv;
@@ -65,6 +66,14 @@ struct AttnArgs {
 
 __device__ __forceinline__ int kappa(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// Key row order for fp8 O^T products: A-operand row i of key tile t holds key
+// 16 t + kappa8(i) of the wave's 64, which puts keys 32 (l / 32) + [0, 32) in
+// lane l's two accumulator tiles (tile t, value v = key 32 (l / 32) + 16 t + v):
+// exactly the 32-byte k-slice of the fp8 B operand, in order.
+__device__ __forceinline__ int kappa8(int r) {
+  return (r & 3) | ((r >> 3) << 2) | (((r >> 2) & 1) << 5);
 }
 
 // The hardware hands workgroup i to XCD i % 8 (MI355X has 8 XCDs, each with
@@ -142,23 +151,37 @@ __device__ __forceinline__ float max_halves(float x) {
   return max3f(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
 }
 
+// Operand modes: bf16 products; mix (fp8 E4M3 S^T = K Q^T, bf16 O^T); fp8
+// (both products on E4M3 codes).
+template <int PREC>
+struct Prec {
+  static constexpr bool QK8 = PREC != RF_PREC_BF16;  // S^T on E4M3 codes
+  static constexpr bool V8 = PREC == RF_PREC_FP8;    // O^T on E4M3 codes
+};
+
 // Operand schedule of one MFMA interval: the S^T products of this block
 // (A = K rows from LDS) followed by the O^T products of the previous block
 // (A = V^T rows from LDS). Every LDS read is one 16-byte fragment per lane;
-// an fp8 S^T product takes two.
-template <int D, bool MIX>
+// an fp8 product takes two.
+template <int D, int PREC>
 struct MfmaPlan {
+  static constexpr bool QK8 = Prec<PREC>::QK8, V8 = Prec<PREC>::V8;
   static constexpr int DT = D / 32;
-  static constexpr int QK_STEPS = MIX ? D / 64 : D / 16;
-  static constexpr int S_RPM = MIX ? 2 : 1;          // reads per S^T product
+  static constexpr int QK_STEPS = QK8 ? D / 64 : D / 16;
+  static constexpr int S_RPM = QK8 ? 2 : 1;          // reads per S^T product
   static constexpr int NS_MFMA = 2 * QK_STEPS;       // S^T products (2 key tiles)
   static constexpr int NS_READ = NS_MFMA * S_RPM;
-  static constexpr int NPV = 4 * DT;                 // O^T products (4 k-steps x DT tiles)
-  static constexpr int NREAD = NS_READ + NPV;
+  // O^T products: DT channel tiles x the wave's 64 keys in k-steps of 16
+  // (bf16) or one k-step of 64 (fp8).
+  static constexpr int NPV = V8 ? DT : 4 * DT;
+  static constexpr int PV_RPM = V8 ? 2 : 1;          // reads per O^T product
+  static constexpr int NREAD = NS_READ + NPV * PV_RPM;
   static constexpr int NMFMA = NS_MFMA + NPV;
   static constexpr int NR = 8;                       // fragments in flight
   static constexpr int NPRE = NR < NS_READ ? NR : NS_READ;  // K reads issued before the barrier
-  static constexpr int rend(int m) { return m < NS_MFMA ? (m + 1) * S_RPM : NS_READ + (m - NS_MFMA) + 1; }
+  static constexpr int rend(int m) {
+    return m < NS_MFMA ? (m + 1) * S_RPM : NS_READ + (m - NS_MFMA + 1) * PV_RPM;
+  }
 };
 
 // Ring of fragments in named registers (an array could be placed in scratch).
@@ -178,54 +201,76 @@ __device__ __forceinline__ uint4& ring_slot(FragRing& f) {
   else return f.r7;
 }
 
-template <int D, bool MIX>
+template <int D, int PREC>
 struct MfmaCtx {
-  using P = MfmaPlan<D, MIX>;
+  using P = MfmaPlan<D, PREC>;
   const uint8_t* kbase;  // this lane's first K fragment in the current K buffer
   const uint8_t* vbase;  // this lane's first V^T fragment in the previous block's buffer
   FragRing ring;
   f32x16 s[2];
   f32x16 o[P::DT];
-  bf16x8 qf[MIX ? 1 : P::QK_STEPS];
-  i32x8 qf8[MIX ? P::QK_STEPS : 1];
-  bf16x8 pf16[2][2];
+  bf16x8 qf[P::QK8 ? 1 : P::QK_STEPS];
+  i32x8 qf8[P::QK8 ? P::QK_STEPS : 1];
+  bf16x8 pf16[2][2];              // P^T operands, bf16 O^T products
+  i32x8 pf8;                      // P^T operand (E4M3 codes), fp8 O^T products
+  int vexp;                       // E8M0 scale of the previous block's V (fp8)
+};
+
+// Bytes per row of a K tile and of a V^T tile in global memory, and their
+// padded LDS strides (the padding spreads a wave's 16-byte reads over all
+// banks).
+template <int D, int PREC>
+struct TileGeom {
+  static constexpr int KROW = Prec<PREC>::QK8 ? D : 2 * D;
+  static constexpr int VROW = Prec<PREC>::V8 ? 128 : 256;
+  static constexpr int KSTR = KROW + 16;
+  static constexpr int VSTR = VROW + 16;
 };
 
 // LDS byte offset of read R relative to its base (compile-time).
-template <int D, bool MIX, int R>
-__device__ __forceinline__ const uint8_t* read_addr(const MfmaCtx<D, MIX>& c) {
-  using P = MfmaPlan<D, MIX>;
-  constexpr int KSTR = (MIX ? D : 2 * D) + 16;
-  constexpr int VSTR = 256 + 16;
+template <int D, int PREC, int R>
+__device__ __forceinline__ const uint8_t* read_addr(const MfmaCtx<D, PREC>& c) {
+  using P = MfmaPlan<D, PREC>;
+  using TG = TileGeom<D, PREC>;
   if constexpr (R < P::NS_READ) {
+    // S^T product sm: key tile t (rows 32 t, or 16 t for the fp8 row order),
+    // channel k-step st.
     constexpr int sm = R / P::S_RPM, half = R % P::S_RPM, st = sm / 2, t = sm % 2;
-    return c.kbase + 32 * t * KSTR + (MIX ? 64 * st + 16 * half : 32 * st);
+    constexpr int trow = P::V8 ? 16 : 32;
+    return c.kbase + trow * t * TG::KSTR + (P::QK8 ? 64 * st + 16 * half : 32 * st);
+  } else if constexpr (P::V8) {
+    // O^T product e (channel tile): 32 key bytes of V^T row 32 e + li.
+    constexpr int pr = R - P::NS_READ, e = pr / 2, half = pr % 2;
+    return c.vbase + 32 * e * TG::VSTR + 16 * half;
   } else {
     constexpr int pm = R - P::NS_READ, tu = pm / P::DT, e = pm % P::DT;
-    return c.vbase + 32 * e * VSTR + 2 * (32 * (tu / 2) + 16 * (tu % 2));
+    return c.vbase + 32 * e * TG::VSTR + 2 * (32 * (tu / 2) + 16 * (tu % 2));
   }
 }
 
-template <int D, bool MIX, int R, int END>
-__device__ __forceinline__ void issue_reads(MfmaCtx<D, MIX>& c) {
-  using P = MfmaPlan<D, MIX>;
+template <int D, int PREC, int R, int END>
+__device__ __forceinline__ void issue_reads(MfmaCtx<D, PREC>& c) {
+  using P = MfmaPlan<D, PREC>;
   if constexpr (R < END && R < P::NREAD) {
-    ring_slot<R % P::NR>(c.ring) = *reinterpret_cast<const uint4*>(read_addr<D, MIX, R>(c));
-    issue_reads<D, MIX, R + 1, END>(c);
+    ring_slot<R % P::NR>(c.ring) = *reinterpret_cast<const uint4*>(read_addr<D, PREC, R>(c));
+    issue_reads<D, PREC, R + 1, END>(c);
   }
 }
 
-template <int D, bool MIX, int M, int MEND = MfmaPlan<D, MIX>::NMFMA>
-__device__ __forceinline__ void mfma_steps(MfmaCtx<D, MIX>& c) {
-  using P = MfmaPlan<D, MIX>;
+template <int NR, int R>
+__device__ __forceinline__ i32x8 ring_pair(FragRing& f) {
+  const uint4 x0 = ring_slot<R % NR>(f), x1 = ring_slot<(R + 1) % NR>(f);
+  return i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+}
+
+template <int D, int PREC, int M, int MEND = MfmaPlan<D, PREC>::NMFMA>
+__device__ __forceinline__ void mfma_steps(MfmaCtx<D, PREC>& c) {
+  using P = MfmaPlan<D, PREC>;
   if constexpr (M < MEND) {
     if constexpr (M < P::NS_MFMA) {
       constexpr int st = M / 2, t = M % 2;
-      if constexpr (MIX) {
-        constexpr int r = 2 * M;
-        const uint4 x0 = ring_slot<r % P::NR>(c.ring), x1 = ring_slot<(r + 1) % P::NR>(c.ring);
-        const i32x8 ka = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                          (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      if constexpr (P::QK8) {
+        const i32x8 ka = ring_pair<P::NR, 2 * M>(c.ring);
         c.s[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, c.qf8[st], c.s[t], 0, 0, 0,
                                                                  127, 0, 127);
       } else {
@@ -233,6 +278,12 @@ __device__ __forceinline__ void mfma_steps(MfmaCtx<D, MIX>& c) {
         __builtin_memcpy(&ka, &ring_slot<M % P::NR>(c.ring), 16);
         c.s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, c.qf[st], c.s[t], 0, 0, 0);
       }
+    } else if constexpr (P::V8) {
+      // O^T tile e += 2^(vexp - 127) V^T (E4M3) P^T (E4M3) over the wave's 64 keys.
+      constexpr int e = M - P::NS_MFMA;
+      const i32x8 va = ring_pair<P::NR, P::NS_READ + 2 * e>(c.ring);
+      c.o[e] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, c.pf8, c.o[e], 0, 0, 0, c.vexp,
+                                                               0, 127);
     } else {
       constexpr int pm = M - P::NS_MFMA, tu = pm / P::DT, e = pm % P::DT;
       constexpr int r = P::NS_READ + pm;
@@ -242,11 +293,11 @@ __device__ __forceinline__ void mfma_steps(MfmaCtx<D, MIX>& c) {
     }
     // Refill the slots this product consumed: NR reads stay ahead.
     constexpr int done_before = M == 0 ? 0 : P::rend(M - 1);
-    issue_reads<D, MIX, done_before + P::NR, P::rend(M) + P::NR>(c);
+    issue_reads<D, PREC, done_before + P::NR, P::rend(M) + P::NR>(c);
     // Keep this order: the scheduler would otherwise pull each read down to
     // its use and leave too few in flight.
     __builtin_amdgcn_sched_barrier(0);
-    mfma_steps<D, MIX, M + 1, MEND>(c);
+    mfma_steps<D, PREC, M + 1, MEND>(c);
   }
 }
 
@@ -275,16 +326,21 @@ __device__ __forceinline__ void mfma_steps(MfmaCtx<D, MIX>& c) {
 // loop covers anything but the data it needs.
 //
 // ALL (the dense path, no lists) visits every key block in order.
-template <int D, bool MIX, bool ALL>
+template <int D, int PREC, bool ALL>
 __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
-  using PL = MfmaPlan<D, MIX>;
-  constexpr int KROW = MIX ? D : 2 * D;  // K row bytes in global memory
-  constexpr int KSTR = KROW + 16;        // K row stride in LDS (bytes, padded)
-  constexpr int VSTR = 256 + 16;         // V^T row stride in LDS (bytes, padded)
-  constexpr int DT = D / 32;             // 32-wide channel tiles of O^T
-  constexpr int KCH = KROW / 16;         // 16-byte chunks per K row
-  constexpr int K_CH = 128 * KCH / 256;  // K chunks per thread of the kh = 1 group
-  constexpr int V_CH = D * 16 / 256;     // V^T chunks per thread of the kh = 0 group
+  using PL = MfmaPlan<D, PREC>;
+  using TG = TileGeom<D, PREC>;
+  constexpr bool MIX = PL::QK8;           // E4M3 Q/K (mix and fp8)
+  constexpr bool V8 = PL::V8;             // E4M3 V and P (fp8)
+  constexpr int KROW = TG::KROW;          // K row bytes in global memory
+  constexpr int KSTR = TG::KSTR;          // K row stride in LDS (bytes, padded)
+  constexpr int VROW = TG::VROW;          // V^T row bytes (128 keys)
+  constexpr int VSTR = TG::VSTR;          // V^T row stride in LDS (bytes, padded)
+  constexpr int DT = D / 32;              // 32-wide channel tiles of O^T
+  constexpr int KCH = KROW / 16;          // 16-byte chunks per K row
+  constexpr int VCH = VROW / 16;          // 16-byte chunks per V^T row
+  constexpr int K_CH = 128 * KCH / 256;   // K chunks per thread of the kh = 1 group
+  constexpr int V_CH = D * VCH / 256;     // V^T chunks per thread of the kh = 0 group
   constexpr int NSTG = K_CH > V_CH ? K_CH : V_CH;
   constexpr int KT = 128 * KSTR, VT = D * VSTR;
   constexpr int TILE_BYTES = 2 * KT + 2 * VT;
@@ -311,7 +367,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   const int qrow = 32 * rg + li;
   const bool qvalid = qrow < len;
 
-  MfmaCtx<D, MIX> c;
+  MfmaCtx<D, PREC> c;
   // Q fragment (B operand of S^T = K Q^T): query row qrow, channels by k-step.
   float q_sigma = 1.0f;
   if constexpr (MIX) {
@@ -349,6 +405,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int u = 0; u < 2; ++u) c.pf16[t][u] = bf16x8{};
+  c.pf8 = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int64_t sel_row = ((int64_t)b * g.n_blocks + q) * g.N1 + n;
@@ -359,14 +416,16 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   const uint8_t* kbytes =
       MIX ? a.k8 + ((int64_t)b * g.N2 + nk) * g.S * D
           : reinterpret_cast<const uint8_t*>(a.kp + ((int64_t)b * g.N2 + nk) * g.S * D);
-  const uint8_t* vbytes = reinterpret_cast<const uint8_t*>(
-      a.vpt + ((int64_t)b * g.N2 + nk) * g.n_blocks * (int64_t)D * 128);
+  const uint8_t* vbytes = reinterpret_cast<const uint8_t*>(a.vpt) +
+                          ((int64_t)b * g.N2 + nk) * g.n_blocks * (int64_t)D * VROW;
   const scale_ptr kscale =
       MIX ? (scale_ptr)(a.k_scale + ((int64_t)b * g.N2 + nk) * g.n_blocks) : nullptr;
+  const scale_ptr vscale =
+      V8 ? (scale_ptr)(a.v_scale + ((int64_t)b * g.N2 + nk) * g.n_blocks) : nullptr;
 
   // Tile copies: buffer loads over this (batch, kv head)'s K and V^T.
   const __amdgpu_buffer_rsrc_t rk = raw_buffer(kbytes, (uint32_t)(g.S * KROW));
-  const __amdgpu_buffer_rsrc_t rv = raw_buffer(vbytes, (uint32_t)((int64_t)g.n_blocks * D * 256));
+  const __amdgpu_buffer_rsrc_t rv = raw_buffer(vbytes, (uint32_t)((int64_t)g.n_blocks * D * VROW));
   auto k_tile_off = [&](int32_t jb) -> int {
     int64_t r0;
     int32_t fl;
@@ -389,7 +448,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   }
 #define RF_VST1(BUF, VAR, M)                                                               \
   if constexpr ((M) < V_CH) {                                                              \
-    const int slot_ = (M) * 256 + gt, d_ = slot_ / 16, c_ = slot_ % 16;                    \
+    const int slot_ = (M) * 256 + gt, d_ = slot_ / VCH, c_ = slot_ % VCH;                  \
     *reinterpret_cast<u32x4*>((BUF) + d_ * VSTR + c_ * 16) = VAR;                          \
   }
 // Tile J into the staging registers: K rows (as 16-byte chunks, row-major)
@@ -442,13 +501,16 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   lds_barrier();
   if (kh == 1) lds_barrier();  // the kh = 1 group runs one interval behind
 
-  // This lane's fragment bases: K row 64 kh + kappa(li) (+ 32 t), V^T row li
-  // (+ 32 e) at key column 64 kh + 8 h (+ 16 k-step).
-  const int koff = (64 * kh + kappa(li)) * KSTR + (MIX ? 32 * h : 16 * h);
-  const int voff = li * VSTR + 2 * (64 * kh + 8 * h);
+  // This lane's fragment bases: K row 64 kh + kappa(li) (+ 32 t) (fp8:
+  // kappa8(li) (+ 16 t)), V^T row li (+ 32 e) at key column 64 kh + 8 h
+  // (+ 16 k-step) (fp8: 64 kh + 32 h).
+  const int krow = V8 ? kappa8(li) : kappa(li);
+  const int koff = (64 * kh + krow) * KSTR + (MIX ? 32 * h : 16 * h);
+  const int voff = V8 ? li * VSTR + 64 * kh + 32 * h : li * VSTR + 2 * (64 * kh + 8 * h);
+  c.vexp = 127;
   int par = 0;  // parity of block i: its K tile sits in K buffer par
   c.kbase = kbuf0 + koff;
-  issue_reads<D, MIX, 0, PL::NPRE>(c);
+  issue_reads<D, PREC, 0, PL::NPRE>(c);
   for (int i = 0; i < cnt; ++i) {
     const int32_t j = safe(w0);
     int64_t kr0;
@@ -463,29 +525,29 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     c.vbase = vbuf0 + (par ^ 1) * VT + voff;  // V^T of the previous block
 #pragma unroll
     for (int t = 0; t < 2; ++t) c.s[t] = f32x16{};
-    issue_reads<D, MIX, PL::NPRE, PL::NR>(c);
+    issue_reads<D, PREC, PL::NPRE, PL::NR>(c);
     // The next tile's global loads ride along with the products, one after
     // every NMFMA / 8 of them, so that no wave stalls on a burst of loads.
     {
       const __amdgpu_buffer_rsrc_t rs_ = kh == 0 ? rv : rk;
-      const int so_ = kh == 0 ? jcopy * (D * 256) : k_tile_off(jcopy);
+      const int so_ = kh == 0 ? jcopy * (D * VROW) : k_tile_off(jcopy);
       const int nch_ = kh == 0 ? V_CH : K_CH;
 #define RF_Q(K) ((K) * PL::NMFMA / 8)
-      mfma_steps<D, MIX, 0, RF_Q(1)>(c);
+      mfma_steps<D, PREC, 0, RF_Q(1)>(c);
       RF_GLD1(st0, 0)
-      mfma_steps<D, MIX, RF_Q(1), RF_Q(2)>(c);
+      mfma_steps<D, PREC, RF_Q(1), RF_Q(2)>(c);
       RF_GLD1(st1, 1)
-      mfma_steps<D, MIX, RF_Q(2), RF_Q(3)>(c);
+      mfma_steps<D, PREC, RF_Q(2), RF_Q(3)>(c);
       RF_GLD1(st2, 2)
-      mfma_steps<D, MIX, RF_Q(3), RF_Q(4)>(c);
+      mfma_steps<D, PREC, RF_Q(3), RF_Q(4)>(c);
       RF_GLD1(st3, 3)
-      mfma_steps<D, MIX, RF_Q(4), RF_Q(5)>(c);
+      mfma_steps<D, PREC, RF_Q(4), RF_Q(5)>(c);
       RF_GLD1(st4, 4)
-      mfma_steps<D, MIX, RF_Q(5), RF_Q(6)>(c);
+      mfma_steps<D, PREC, RF_Q(5), RF_Q(6)>(c);
       RF_GLD1(st5, 5)
-      mfma_steps<D, MIX, RF_Q(6), RF_Q(7)>(c);
+      mfma_steps<D, PREC, RF_Q(6), RF_Q(7)>(c);
       RF_GLD1(st6, 6)
-      mfma_steps<D, MIX, RF_Q(7), RF_Q(8)>(c);
+      mfma_steps<D, PREC, RF_Q(7), RF_Q(8)>(c);
       RF_GLD1(st7, 7)
 #undef RF_Q
     }
@@ -510,7 +572,8 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int kv = 64 * kh + 32 * t + 16 * (v / 8) + 8 * h + (v % 8);
+          const int kv = V8 ? 64 * kh + 32 * h + 16 * t + v
+                            : 64 * kh + 32 * t + 16 * (v / 8) + 8 * h + (v % 8);
           if (kv >= klen) c.s[t][v] = -INFINITY;
         }
     }
@@ -531,10 +594,15 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     // hold as well, and the rescale of O is skipped for most blocks. O^T holds
     // every product up to the previous block here, exactly what the rescale
     // must cover.
+    // fp8: P = 2^(t - m_run + 8) goes to E4M3 (largest finite 448), so m_run is
+    // the integer ceiling of the running maximum, raised as soon as a block
+    // exceeds it: the largest P stays in (128, 256], and the rescale by a
+    // power of two is exact and leaves the rounding of normal P unchanged.
     const float mc = mx * cs;
-    if (__any(mc > m_run + 8.0f)) {
-      const float m_new = fmaxf(m_run, mc);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    if (__any(mc > m_run + (V8 ? 0.0f : 8.0f))) {
+      const float m_new = fmaxf(m_run, V8 ? ceilf(mc) : mc);
+      const float alpha = V8 ? (m_run == -INFINITY ? 0.0f : ldexpf(1.0f, (int)(m_run - m_new)))
+                             : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -544,25 +612,45 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     }
     // While every key so far is masked m_run is -inf; any finite stand-in keeps
     // exp2(-inf - m) at 0 instead of NaN.
-    const float mneg = -fmaxf(m_run, -1e30f);
+    const float mneg = (V8 ? 8.0f : 0.0f) - fmaxf(m_run, -1e30f);
 
     float lsum = 0.0f;
+    if constexpr (V8) {
+      // P as E4M3 codes (round to nearest even; P <= 2^8 < 448), byte 16 t + v
+      // of the B operand; the row sum adds the rounded values (they are what
+      // multiplies V).
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int w = 0; w < 8; ++w) {
+        const int t = w / 4, v0 = 4 * (w % 4);
+        float p[4];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+        for (int x = 0; x < 4; ++x) p[x] = __builtin_amdgcn_exp2f(fmaf(c.s[t][v0 + x], cs, mneg));
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], pk, true);
+        c.pf8[w] = pk;
+        const auto r0 = __builtin_amdgcn_cvt_pk_f32_fp8(pk, false);
+        const auto r1 = __builtin_amdgcn_cvt_pk_f32_fp8(pk, true);
+        lsum += (r0[0] + r0[1]) + (r1[0] + r1[1]);
+      }
+      c.vexp = (int)((__float_as_uint(vscale[j]) >> 23) & 0xffu);
+    } else {
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(c.s[t][8 * u + m], cs, mneg));
-          lsum += p;
-          c.pf16[t][u][m] = (__bf16)p;
-        }
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(c.s[t][8 * u + m], cs, mneg));
+            lsum += p;
+            c.pf16[t][u][m] = (__bf16)p;
+          }
+    }
     l_run += lsum;
 
     // First K fragments of block i + 1 (written at least one interval ago).
     par ^= 1;
     c.kbase = kbuf0 + par * KT + koff;
-    issue_reads<D, MIX, 0, PL::NPRE>(c);
+    issue_reads<D, PREC, 0, PL::NPRE>(c);
     lds_barrier();
     w0 = w1;
     w1 = w2;
@@ -572,16 +660,28 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   // O^T += V^T P^T of the last block.
   if (cnt > 0) {
     const uint8_t* vs = vbuf0 + (par ^ 1) * VT + voff;
+    if constexpr (V8) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int e = 0; e < DT; ++e) {
+        const uint4 x0 = *reinterpret_cast<const uint4*>(vs + 32 * e * VSTR);
+        const uint4 x1 = *reinterpret_cast<const uint4*>(vs + 32 * e * VSTR + 16);
+        const i32x8 va = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                          (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        c.o[e] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, c.pf8, c.o[e], 0, 0, 0, c.vexp,
+                                                                 0, 127);
+      }
+    } else {
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int e = 0; e < DT; ++e) {
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(
-              vs + 32 * e * VSTR + 2 * (32 * t + 16 * u));
-          c.o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, c.pf16[t][u], c.o[e], 0, 0, 0);
-        }
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < DT; ++e) {
+            const bf16x8 va = *reinterpret_cast<const bf16x8*>(
+                vs + 32 * e * VSTR + 2 * (32 * t + 16 * u));
+            c.o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, c.pf16[t][u], c.o[e], 0, 0, 0);
+          }
+    }
   }
   if (kh == 0) lds_barrier();  // matches the kh = 1 group's extra barrier
 
@@ -639,8 +739,11 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
 rf_status rf_launch_sparse_attn(const RfGeom& g, int32_t precision, float scale, const void* qp,
                                 const void* kp, const void* vpt, const uint8_t* q8,
                                 const uint8_t* k8, const float* q_scale, const float* k_scale,
-                                const int32_t* select_idx, const int32_t* select_num,
-                                int32_t max_kv, void* out_p, void* stream) {
+                                const float* v_scale, const int32_t* select_idx,
+                                const int32_t* select_num, int32_t max_kv, void* out_p,
+                                void* stream) {
+  if (precision != RF_PREC_BF16 && precision != RF_PREC_MIX && precision != RF_PREC_FP8)
+    return RF_ERR_PRECISION;
   AttnArgs a;
   a.g = g;
   a.scale_log2 = scale * kLog2e;
@@ -651,6 +754,7 @@ rf_status rf_launch_sparse_attn(const RfGeom& g, int32_t precision, float scale,
   a.k8 = k8;
   a.q_scale = q_scale;
   a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.select_idx = select_idx;
   a.select_num = select_num;
   a.max_kv = max_kv;
@@ -659,19 +763,21 @@ rf_status rf_launch_sparse_attn(const RfGeom& g, int32_t precision, float scale,
   if (wgs > 0x7fffffff) return RF_ERR_SHAPE;
   // Tile loads address one (batch, kv head)'s K and V^T through 32-bit buffer
   // offsets.
-  const int64_t krow = precision == RF_PREC_MIX ? g.D : 2 * g.D;
-  if (g.S * krow > 0x7fffffff || (int64_t)g.n_blocks * g.D * 256 > 0x7fffffff) return RF_ERR_SHAPE;
+  const int64_t krow = precision == RF_PREC_BF16 ? 2 * g.D : g.D;
+  const int64_t vrow = precision == RF_PREC_FP8 ? 128 : 256;
+  if (g.S * krow > 0x7fffffff || (int64_t)g.n_blocks * g.D * vrow > 0x7fffffff) return RF_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((uint32_t)wgs);
-  const bool mix = precision == RF_PREC_MIX;
   const bool all = select_idx == nullptr;
   // One instantiation per (head_dim, precision, lists or none).
   using Kern = void (*)(AttnArgs);
-  static const Kern kernels[2][2][2] = {
-      {{sparse_attn_kernel<64, false, false>, sparse_attn_kernel<64, false, true>},
-       {sparse_attn_kernel<64, true, false>, sparse_attn_kernel<64, true, true>}},
-      {{sparse_attn_kernel<128, false, false>, sparse_attn_kernel<128, false, true>},
-       {sparse_attn_kernel<128, true, false>, sparse_attn_kernel<128, true, true>}}};
-  hipLaunchKernelGGL(kernels[g.D == 128][mix][all], grid, dim3(kThreads8), 0, s, a);
+  static const Kern kernels[2][3][2] = {
+      {{sparse_attn_kernel<64, RF_PREC_BF16, false>, sparse_attn_kernel<64, RF_PREC_BF16, true>},
+       {sparse_attn_kernel<64, RF_PREC_MIX, false>, sparse_attn_kernel<64, RF_PREC_MIX, true>},
+       {sparse_attn_kernel<64, RF_PREC_FP8, false>, sparse_attn_kernel<64, RF_PREC_FP8, true>}},
+      {{sparse_attn_kernel<128, RF_PREC_BF16, false>, sparse_attn_kernel<128, RF_PREC_BF16, true>},
+       {sparse_attn_kernel<128, RF_PREC_MIX, false>, sparse_attn_kernel<128, RF_PREC_MIX, true>},
+       {sparse_attn_kernel<128, RF_PREC_FP8, false>, sparse_attn_kernel<128, RF_PREC_FP8, true>}}};
+  hipLaunchKernelGGL(kernels[g.D == 128][precision][all], grid, dim3(kThreads8), 0, s, a);
   return hipGetLastError() == hipSuccess ? RF_OK : RF_ERR_HIP;
 }

@@ -97,7 +97,7 @@ rf_status rf_derive(const rf_desc* d, RfGeom* g, rf_plan_info* info);
 rf_status rf_launch_permute(const RfGeom& g, int32_t precision, const void* q, const void* k,
                             const void* v, void* qp, void* kp, void* vpt, float* q_pool,
                             float* k_pool, uint8_t* q8, uint8_t* k8, float* q_scale,
-                            float* k_scale, void* stream);
+                            float* k_scale, float* v_scale, void* stream);
 rf_status rf_launch_unpermute(const RfGeom& g, const void* out_p, void* out, void* stream);
 rf_status rf_launch_pool_select(const RfGeom& g, float scale, const void* qp, const void* kp,
                                 const float* q_pool, const float* k_pool, int32_t* select_idx,
@@ -105,8 +105,9 @@ rf_status rf_launch_pool_select(const RfGeom& g, float scale, const void* qp, co
 rf_status rf_launch_sparse_attn(const RfGeom& g, int32_t precision, float scale, const void* qp,
                                 const void* kp, const void* vpt, const uint8_t* q8,
                                 const uint8_t* k8, const float* q_scale, const float* k_scale,
-                                const int32_t* select_idx, const int32_t* select_num,
-                                int32_t max_kv, void* out_p, void* stream);
+                                const float* v_scale, const int32_t* select_idx,
+                                const int32_t* select_num, int32_t max_kv, void* out_p,
+                                void* stream);
 
 // Workspace layout of rf_pool_select (bytes, 256-aligned pieces):
 // scores [B, N1, nS, nS] f32, then q_pool [B, N1, nS, D] f32, then k_pool [B, N2, nS, D] f32.

@@ -40,6 +40,7 @@ struct PermuteArgs {
   uint8_t* k8;
   float* q_scale;
   float* k_scale;
+  float* v_scale;  // fp8 precision: V as E4M3 codes (vpt) with power-of-two scales
 };
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -59,6 +60,17 @@ __device__ __forceinline__ uint32_t e4m3_rne(float y) {
   const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);  // keep 3 mantissa bits, ties to even
   const uint32_t e = (r >> 23) - 127u + 7u;
   return sign | (e << 3) | ((r >> 20) & 7u);
+}
+
+// Smallest e with amax <= 448 * 2^e, clamped to [-126, 127] (a normal fp32
+// power of two); 0 for amax == 0. With amax = f * 2^x, f in [0.5, 1), and
+// 448 = 0.875 * 2^9: e = x - 9 if f <= 0.875, else x - 8 (exact).
+__device__ __forceinline__ int pow2_scale_exp(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int x;
+  const float f = frexpf(amax, &x);
+  const int e = f <= 0.875f ? x - 9 : x - 8;
+  return e < -126 ? -126 : (e > 127 ? 127 : e);
 }
 
 // Block-wide reductions over 256 threads through LDS, fixed order.
@@ -128,6 +140,49 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
   if (kind == 2) {
     // V: stage the block in LDS, then write it transposed [D][128] with zero
     // columns past the block's length.
+    if (a.v_scale) {
+      // fp8: E4M3 codes of x / 2^e with the block's power-of-two scale 2^e
+      // (exact scaling), same transposed layout in bytes.
+      float amax = 0.0f;
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        const uint32_t w[4] = {val[p].x, val[p].y, val[p].z, val[p].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          amax = fmaxf(amax, fmaxf(fabsf(bf_lo(w[e])), fabsf(bf_hi(w[e]))));
+      }
+      amax = block_max(amax, red);
+      const int ex = pow2_scale_exp(amax);
+      const float inv = ldexpf(1.0f, -ex);
+      uint16_t* tile = reinterpret_cast<uint16_t*>(red);  // [128][D + 8]
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        const int i = p * RPP + rsub;
+        *reinterpret_cast<uint4*>(tile + i * (D + 8) + c * 8) = val[p];
+      }
+      __syncthreads();
+      uint8_t* dst = reinterpret_cast<uint8_t*>(a.vpt) +
+                     (((int64_t)b * g.N2 + n) * g.n_blocks + j) * (int64_t)D * 128;
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m) {
+        const int qd = tid + kThreads * m;
+        const int d = qd / 8, cc = qd % 8;  // channel d, keys [16 cc, 16 cc + 16)
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t x = 0;
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            const float f = __uint_as_float((uint32_t)tile[(cc * 16 + 4 * e + bb) * (D + 8) + d] << 16);
+            x |= e4m3_rne(f * inv) << (8 * bb);
+          }
+          w[e] = x;
+        }
+        *reinterpret_cast<uint4*>(dst + d * 128 + cc * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      if (tid == 0) a.v_scale[((int64_t)b * g.N2 + n) * g.n_blocks + j] = ldexpf(1.0f, ex);
+      return;
+    }
     uint16_t* tile = reinterpret_cast<uint16_t*>(red);  // [128][D + 8]
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
@@ -267,7 +322,7 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(UnpermuteArgs a) {
 rf_status rf_launch_permute(const RfGeom& g, int32_t precision, const void* q, const void* k,
                             const void* v, void* qp, void* kp, void* vpt, float* q_pool,
                             float* k_pool, uint8_t* q8, uint8_t* k8, float* q_scale,
-                            float* k_scale, void* stream) {
+                            float* k_scale, float* v_scale, void* stream) {
   (void)precision;
   PermuteArgs a;
   a.g = g;
@@ -283,6 +338,7 @@ rf_status rf_launch_permute(const RfGeom& g, int32_t precision, const void* q, c
   a.k8 = k8;
   a.q_scale = q_scale;
   a.k_scale = k_scale;
+  a.v_scale = v_scale;
   const dim3 grid(g.n_blocks, g.B * (g.N1 + 2 * g.N2));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (g.D == 128)

@@ -45,7 +45,7 @@ class RfPlanInfo(ctypes.Structure):
         ("qp_elems", ctypes.c_int64), ("kp_elems", ctypes.c_int64), ("vpt_elems", ctypes.c_int64),
         ("q_pool_elems", ctypes.c_int64), ("k_pool_elems", ctypes.c_int64),
         ("q_scale_elems", ctypes.c_int64), ("k_scale_elems", ctypes.c_int64),
-        ("ws_select_bytes", ctypes.c_size_t),
+        ("v_scale_elems", ctypes.c_int64), ("ws_select_bytes", ctypes.c_size_t),
     ]
 
     def as_dict(self):
@@ -70,10 +70,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P = ctypes.c_void_p
     D = ctypes.POINTER(RfDesc)
     lib.rf_plan.argtypes = [D, ctypes.POINTER(RfPlanInfo)]
-    lib.rf_permute.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.rf_permute.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.rf_pool_select.argtypes = [D, P, P, P, P, P, P, ctypes.c_int32, P, ctypes.c_size_t, P]
-    lib.rf_sparse_attn.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, P]
-    lib.rf_dense_attn.argtypes = [D, P, P, P, P, P, P, P, P, P]
+    lib.rf_sparse_attn.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, P]
+    lib.rf_dense_attn.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
     lib.rf_unpermute.argtypes = [D, P, P, P]
     for f in ("rf_plan", "rf_permute", "rf_pool_select", "rf_sparse_attn", "rf_dense_attn",
               "rf_unpermute"):
@@ -169,11 +169,12 @@ def _stream(stream) -> Optional[int]:
 
 
 def rf_permute(desc: Desc, q, k, v, qp=None, kp=None, vpt=None, q_pool=None, k_pool=None,
-               q8=None, k8=None, q_scale=None, k_scale=None, stream=None):
+               q8=None, k8=None, q_scale=None, k_scale=None, v_scale=None, stream=None):
     d = desc.c()
     _check("rf_permute", load_library().rf_permute(
         ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(qp), _ptr(kp), _ptr(vpt), _ptr(q_pool),
-        _ptr(k_pool), _ptr(q8), _ptr(k8), _ptr(q_scale), _ptr(k_scale), _stream(stream)))
+        _ptr(k_pool), _ptr(q8), _ptr(k8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+        _stream(stream)))
 
 
 def rf_pool_select(desc: Desc, qp, kp, q_pool, k_pool, select_idx, select_num, max_kv: int,
@@ -186,20 +187,21 @@ def rf_pool_select(desc: Desc, qp, kp, q_pool, k_pool, select_idx, select_num, m
         _ptr(select_num), int(max_kv), _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
-def rf_sparse_attn(desc: Desc, qp, kp, vpt, q8, k8, q_scale, k_scale, select_idx, select_num,
-                   max_kv: int, out_p, stream=None):
+def rf_sparse_attn(desc: Desc, qp, kp, vpt, q8, k8, q_scale, k_scale, v_scale, select_idx,
+                   select_num, max_kv: int, out_p, stream=None):
     d = desc.c()
     _check("rf_sparse_attn", load_library().rf_sparse_attn(
         ctypes.byref(d), _ptr(qp), _ptr(kp), _ptr(vpt), _ptr(q8), _ptr(k8), _ptr(q_scale),
-        _ptr(k_scale), _ptr(select_idx), _ptr(select_num), int(max_kv), _ptr(out_p),
-        _stream(stream)))
+        _ptr(k_scale), _ptr(v_scale), _ptr(select_idx), _ptr(select_num), int(max_kv),
+        _ptr(out_p), _stream(stream)))
 
 
-def rf_dense_attn(desc: Desc, qp, kp, vpt, q8, k8, q_scale, k_scale, out_p, stream=None):
+def rf_dense_attn(desc: Desc, qp, kp, vpt, q8, k8, q_scale, k_scale, v_scale, out_p,
+                  stream=None):
     d = desc.c()
     _check("rf_dense_attn", load_library().rf_dense_attn(
         ctypes.byref(d), _ptr(qp), _ptr(kp), _ptr(vpt), _ptr(q8), _ptr(k8), _ptr(q_scale),
-        _ptr(k_scale), _ptr(out_p), _stream(stream)))
+        _ptr(k_scale), _ptr(v_scale), _ptr(out_p), _stream(stream)))
 
 
 def rf_unpermute(desc: Desc, out_p, out, stream=None):
@@ -213,6 +215,9 @@ class Buffers:
 
     ``lists=False`` leaves out what only the sparse path uses (pooled blocks,
     selectIdx / selectNum, the selection workspace): the dense path needs none.
+    In mix and fp8 precision Q/K exist only as E4M3 codes (``q8``, ``k8``) with
+    per-block scales; in fp8 ``vpt`` holds one-byte E4M3 codes and ``v_scale``
+    their power-of-two block scales.
     """
 
     def __init__(self, desc: Desc, device="cuda", lists: bool = True):
@@ -222,10 +227,12 @@ class Buffers:
         B, N1, N2, S, D = desc.batch, desc.heads_q, desc.heads_kv, desc.seq_len, desc.head_dim
         nB, nS = info.n_blocks, info.n_sparse
         bf = torch.bfloat16
-        mix = desc.precision == "mix"
+        mix = desc.precision in ("mix", "fp8", PREC_MIX, PREC_FP8)   # E4M3 Q/K
+        v8 = desc.precision in ("fp8", PREC_FP8)                       # E4M3 V
         self.qp = None if mix else torch.empty((B, N1, S, D), dtype=bf, device=device)
         self.kp = None if mix else torch.empty((B, N2, S, D), dtype=bf, device=device)
-        self.vpt = torch.empty((B, N2, nB, D, 128), dtype=bf, device=device)
+        self.vpt = torch.empty((B, N2, nB, D, 128), dtype=torch.uint8 if v8 else bf, device=device)
+        self.v_scale = torch.empty((B, N2, nB), dtype=torch.float32, device=device) if v8 else None
         f32 = torch.float32
         self.q_pool = torch.empty((B, N1, nS, D), dtype=f32, device=device) if lists else None
         self.k_pool = torch.empty((B, N2, nS, D), dtype=f32, device=device) if lists else None
@@ -255,12 +262,12 @@ def attention(q, k, v, desc: Desc, bufs: Optional[Buffers] = None, out=None, str
         out = torch.empty_like(q)
     b = bufs
     rf_permute(desc, q, k, v, b.qp, b.kp, b.vpt, b.q_pool, b.k_pool, b.q8, b.k8, b.q_scale,
-               b.k_scale, stream=stream)
+               b.k_scale, b.v_scale, stream=stream)
     nB = b.info.n_blocks
     rf_pool_select(desc, b.qp, b.kp, b.q_pool, b.k_pool, b.select_idx, b.select_num, nB,
                    b.workspace, stream=stream)
-    rf_sparse_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, b.select_idx,
-                   b.select_num, nB, b.out_p, stream=stream)
+    rf_sparse_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, b.v_scale,
+                   b.select_idx, b.select_num, nB, b.out_p, stream=stream)
     rf_unpermute(desc, b.out_p, out, stream=stream)
     return out, bufs
 
@@ -270,8 +277,8 @@ def dense_attention(q, k, v, desc: Desc, bufs: Optional[Buffers] = None, out=Non
 
     Same inputs and output as ``attention``; no pooling, no selection, no
     lists. Full attention is independent of the key order, so the result is
-    full attention in the caller's order (for mix precision: with the same
-    per-block E4M3 Q/K as the sparse path).
+    full attention in the caller's order (for mix and fp8 precision: with the
+    same per-block E4M3 operands as the sparse path).
     """
     import torch
     if bufs is None:
@@ -280,8 +287,8 @@ def dense_attention(q, k, v, desc: Desc, bufs: Optional[Buffers] = None, out=Non
         out = torch.empty_like(q)
     b = bufs
     rf_permute(desc, q, k, v, b.qp, b.kp, b.vpt, None, None, b.q8, b.k8, b.q_scale, b.k_scale,
-               stream=stream)
-    rf_dense_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, b.out_p,
-                  stream=stream)
+               b.v_scale, stream=stream)
+    rf_dense_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, b.v_scale,
+                  b.out_p, stream=stream)
     rf_unpermute(desc, b.out_p, out, stream=stream)
     return out, bufs

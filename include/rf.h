@@ -6,7 +6,7 @@
  * plan:
  *   rf_plan         host: validate a call, derive the arrangement and sizes
  *   rf_permute      arrange Q/K/V into 128-token space-time blocks, pool the
- *                   sparse blocks, and (mix precision) quantise Q/K to fp8
+ *                   sparse blocks, and (mix, fp8 precision) quantise to fp8
  *   rf_pool_select  score pooled blocks and build selectIdx / selectNum
  *   rf_sparse_attn  exact softmax attention restricted to the listed blocks
  *   rf_dense_attn   the same attention over every block (the dense path)
@@ -23,6 +23,9 @@
  *   [RF2]  "RainFusion2.0: Temporal-Spatial Awareness and Hardware-Efficient
  *          Block-wise Sparse Attention": abstract (block-mean representative
  *          tokens, spatiotemporal permutation, first-frame sink).
+ *   [MXA]  "MXAttention: Data-Free Optimal Scaling and Pre-Normalization
+ *          Quantization for MXFP4 Attention" (catalyzex author page):
+ *          abstract (softmax exponentials quantised before the row sum).
  *
  * Conventions for every entry point:
  *   - The caller owns all memory. Device pointers point to HIP device memory
@@ -79,7 +82,15 @@ typedef enum rf_precision {
   RF_PREC_MIX = 1,  /* Q/K as fp8 E4M3 with one fp32 scale per (batch, head, 128-row
                        block); V, probabilities and output bf16; fp32 softmax.
                        [RFA] Configuration names "mix" without defining it. */
-  RF_PREC_FP8 = 2   /* all-fp8 mode named by [RFA]; not built: RF_ERR_UNSUPPORTED */
+  RF_PREC_FP8 = 2   /* all operands E4M3. [RFA] Configuration names "fp8" without defining it.
+                       Q/K as in mix; V per (batch, kv head, 128-row block) with a
+                       power-of-two scale 2^e, e the smallest integer with
+                       amax <= 448 * 2^e (clamped to [-126, 127]; 0 for a zero block),
+                       code = E4M3(x / 2^e); probabilities P = E4M3(2^(t - M + 8)) with
+                       t = scale*<q,k>/ln 2 and M = ceil(row max of t) (largest P in
+                       (128, 256]), and
+                       out = sum P v / sum P (the sum of the rounded P; [MXA]).
+                       Softmax bookkeeping and accumulation fp32, output bf16. */
 } rf_precision;
 
 /* One attention call. Sizes are per batch item; all batch items share the
@@ -120,11 +131,13 @@ typedef struct rf_plan_info {
   int64_t promoted_rows;    /* video rows moved to the dense tail ([RFA] Geometry handling) */
   int64_t qp_elems;         /* bf16 elements of qp / out_p: batch*heads_q*seq_len*head_dim */
   int64_t kp_elems;         /* bf16 elements of kp: batch*heads_kv*seq_len*head_dim */
-  int64_t vpt_elems;        /* bf16 elements of vpt: batch*heads_kv*n_blocks*head_dim*128 */
+  int64_t vpt_elems;        /* elements of vpt: batch*heads_kv*n_blocks*head_dim*128
+                               (bf16; one-byte E4M3 codes in fp8 precision) */
   int64_t q_pool_elems;     /* fp32 elements of q_pool: batch*heads_q*n_sparse*head_dim */
   int64_t k_pool_elems;     /* fp32 elements of k_pool: batch*heads_kv*n_sparse*head_dim */
   int64_t q_scale_elems;    /* fp32 elements of q_scale (mix): batch*heads_q*n_blocks */
   int64_t k_scale_elems;    /* fp32 elements of k_scale (mix): batch*heads_kv*n_blocks */
+  int64_t v_scale_elems;    /* fp32 elements of v_scale (fp8): batch*heads_kv*n_blocks */
   size_t ws_select_bytes;   /* workspace of rf_pool_select */
 } rf_plan_info;
 
@@ -132,7 +145,7 @@ typedef struct rf_plan_info {
  * so it can run on a machine without a GPU. */
 rf_status rf_plan(const rf_desc* desc, rf_plan_info* info);
 
-/* Step 1 (+ pooling, + mix quantisation). [RFA] introduction and Geometry
+/* Step 1 (+ pooling, + fp8 quantisation). [RFA] introduction and Geometry
  * handling; [XPR] commit summary (frame pairs, one call for Q, K and V);
  * [RF2] abstract (spatiotemporal permutation, block means).
  *
@@ -152,14 +165,21 @@ rf_status rf_plan(const rf_desc* desc, rf_plan_info* info);
  *          Required when v is given (it is the layout rf_sparse_attn reads).
  *   q_pool fp32 [B, N1, n_sparse, D] mean of each sparse block of Q
  *   k_pool fp32 [B, N2, n_sparse, D] mean of each sparse block of K
- *   q8,k8  uint8 E4M3 codes, same shape as qp/kp   (mix; required in mix mode)
- *   q_scale,k_scale fp32 [B, N, n_blocks] per-block scales (mix; required)
+ *   q8,k8  uint8 E4M3 codes, same shape as qp/kp   (mix, fp8; required there)
+ *   q_scale,k_scale fp32 [B, N, n_blocks] per-block scales (mix, fp8; required)
+ *   v_scale fp32 [B, N2, n_blocks] power-of-two V scales (fp8; required when v
+ *          is given; ignored otherwise). In fp8 precision vpt holds one-byte
+ *          E4M3 codes of V / v_scale in the same block-transposed layout.
  * Mix quantisation of a block: amax = max |x|; r = 448.0f / amax;
  * code = E4M3 round-to-nearest-even, saturating at 448, of (float)(x * r);
- * scale = amax / 448.0f; an all-zero block gets r = scale = 1. */
+ * scale = amax / 448.0f; an all-zero block gets r = scale = 1.
+ * Errors: RF_ERR_NULL (a given input has no output), RF_ERR_PRECISION (a
+ * buffer the precision needs is NULL), RF_ERR_ALIAS (an output overlaps an
+ * input), plus the descriptor errors of rf_plan. */
 rf_status rf_permute(const rf_desc* desc, const void* q, const void* k, const void* v,
                      void* qp, void* kp, void* vpt, float* q_pool, float* k_pool,
-                     uint8_t* q8, uint8_t* k8, float* q_scale, float* k_scale, void* stream);
+                     uint8_t* q8, uint8_t* k8, float* q_scale, float* k_scale, float* v_scale,
+                     void* stream);
 
 /* Steps 2-3. [RFA] introduction (pool 128-token blocks, rank per query
  * block, keep the highest-scoring); [RF2] abstract (block means as
@@ -186,7 +206,9 @@ rf_status rf_pool_select(const rf_desc* desc, const void* qp, const void* kp,
  * the listed 128x128 blocks (no additive mask; short blocks contribute only
  * their real rows). fp32 accumulation and fp32 online softmax.
  * bf16 precision reads qp, kp, vpt; mix precision reads q8, k8, q_scale,
- * k_scale, vpt (logits = scale * q_scale * k_scale * <q8, k8>).
+ * k_scale, vpt (logits = scale * q_scale * k_scale * <q8, k8>); fp8 precision
+ * also reads v_scale, with vpt as E4M3 codes, and quantises P (see
+ * RF_PREC_FP8). Arguments a precision does not read may be NULL.
  * select_idx / select_num as above (any list the caller builds is accepted:
  * entries outside [0, n_blocks) contribute nothing, exactly as if skipped,
  * provided V holds finite values; counts are clamped to max_kv).
@@ -194,7 +216,7 @@ rf_status rf_pool_select(const rf_desc* desc, const void* qp, const void* kp,
  * out_p: bf16 [B, N1, S, D], permuted row order, rounded to nearest even. */
 rf_status rf_sparse_attn(const rf_desc* desc, const void* qp, const void* kp, const void* vpt,
                          const uint8_t* q8, const uint8_t* k8, const float* q_scale,
-                         const float* k_scale, const int32_t* select_idx,
+                         const float* k_scale, const float* v_scale, const int32_t* select_idx,
                          const int32_t* select_num, int32_t max_kv, void* out_p, void* stream);
 
 /* Dense path. [RFA] introduction: calls that RainFusion does not handle, and
@@ -209,7 +231,7 @@ rf_status rf_sparse_attn(const rf_desc* desc, const void* qp, const void* kp, co
  * out_p: bf16 [B, N1, S, D], permuted row order, rounded to nearest even. */
 rf_status rf_dense_attn(const rf_desc* desc, const void* qp, const void* kp, const void* vpt,
                         const uint8_t* q8, const uint8_t* k8, const float* q_scale,
-                        const float* k_scale, void* out_p, void* stream);
+                        const float* k_scale, const float* v_scale, void* out_p, void* stream);
 
 /* Step 5. [XPR] commit summary (inverse rearrange; roundtrip check).
  * out[natural row pi(r)] = out_p[r]; out in the caller's layout with heads_q

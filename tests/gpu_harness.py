@@ -11,7 +11,10 @@ Comparison rules:
   sums is not fixed);
 * pooled means: |gpu - oracle| <= 2e-6 (fp32 sums of 128 bf16 values);
 * attention output: max-abs <= 2e-2 and mean-abs <= 2e-3 against the float64
-  oracle (bf16), 6e-2 / 6e-3 for the mix precision.
+  oracle (bf16), 6e-2 / 6e-3 for the mix precision;
+* fp8 precision: 2e-2 / 2e-3 against the oracle's fp8 reading on the same
+  codes (FP8_TOL), 1.2e-1 / 1.2e-2 against the unquantised oracle
+  (FP8_E2E_TOL: the mix bound doubled, for V and P rounded to E4M3 as well).
 """
 from __future__ import annotations
 
@@ -26,6 +29,8 @@ from synth import bf16_to_f32
 
 BF16_TOL = (2e-2, 2e-3)
 MIX_TOL = (6e-2, 6e-3)
+FP8_TOL = (2e-2, 2e-3)
+FP8_E2E_TOL = (1.2e-1, 1.2e-2)
 NEAR_TIE_REL = 1e-5
 
 
@@ -63,9 +68,10 @@ def run_gpu(desc, q, k, v):
 
 
 def expected_vpt(vp_u16, p, D):
-    """Block-transposed V ``[B, N, nB, D, 128]`` (zero past a short block)."""
+    """Block-transposed V ``[B, N, nB, D, 128]`` (zero past a short block); bf16
+    bit patterns, or E4M3 codes in fp8 precision (same element type as the input)."""
     B, N = vp_u16.shape[:2]
-    out = np.zeros((B, N, p.n_blocks, D, 128), dtype=np.uint16)
+    out = np.zeros((B, N, p.n_blocks, D, 128), dtype=vp_u16.dtype)
     for j, (r0, n) in enumerate(p.blocks):
         out[:, :, j, :, :n] = vp_u16[:, :, r0:r0 + n, :].transpose(0, 1, 3, 2)
     return out

@@ -99,7 +99,6 @@ BAD = [
     ("geometry_len", dict(seq_len=4737), 8),
     ("geometry_ff", dict(first_frame_rows=100), 8),
     ("geometry_grid", dict(grid=(9, 0, 32)), 8),
-    ("precision_fp8", dict(precision="fp8"), 10),
     ("precision_bad", dict(precision=9), 11),
 ]
 
@@ -117,13 +116,13 @@ def test_invalid_descriptors(name, change, status):
     c = d.c()
     fake = ctypes.c_void_p(0x1000)
     assert lib.rf_permute(ctypes.byref(c), fake, fake, fake, fake, fake, fake, None, None, None,
-                          None, None, None, None) == status
+                          None, None, None, None, None) == status
     assert lib.rf_pool_select(ctypes.byref(c), fake, fake, None, None, fake, fake, 1000, fake,
                               1 << 30, None) == status
-    assert lib.rf_sparse_attn(ctypes.byref(c), fake, fake, fake, None, None, None, None, fake,
-                              fake, 1000, fake, None) == status
-    assert lib.rf_dense_attn(ctypes.byref(c), fake, fake, fake, None, None, None, None, fake,
-                             None) == status
+    assert lib.rf_sparse_attn(ctypes.byref(c), fake, fake, fake, None, None, None, None, None,
+                              fake, fake, 1000, fake, None) == status
+    assert lib.rf_dense_attn(ctypes.byref(c), fake, fake, fake, None, None, None, None, None,
+                             fake, None) == status
     assert lib.rf_unpermute(ctypes.byref(c), fake, fake, None) == status
 
 
@@ -146,10 +145,18 @@ def test_argument_errors_before_launch():
     assert lib.rf_plan(ctypes.byref(c), None) == 1
     # rf_permute: V without its block-transposed output.
     assert lib.rf_permute(ctypes.byref(c), None, None, a, None, None, None, None, None, None,
-                          None, None, None, None) == 1
+                          None, None, None, None, None) == 1
     # rf_permute: output overlapping its input.
     assert lib.rf_permute(ctypes.byref(c), a, None, None, a, None, None, None, None, None, None,
-                          None, None, None) == 13
+                          None, None, None, None) == 13
+    # rf_permute in fp8: V without its power-of-two scales; Q without its codes.
+    d8 = _good()
+    d8.precision = "fp8"
+    c8 = d8.c()
+    assert lib.rf_permute(ctypes.byref(c8), None, None, a, None, None, b2, None, None, None,
+                          None, None, None, None, None) == 11
+    assert lib.rf_permute(ctypes.byref(c8), a, None, None, b2, None, None, None, None, None,
+                          None, None, None, None, None) == 11
     # rf_pool_select: workspace too small, NULL workspace, narrow selectIdx.
     assert lib.rf_pool_select(ctypes.byref(c), a, b2, None, None, c3, d4, info.n_blocks, e5,
                               info.ws_select_bytes - 1, None) == 9
@@ -161,15 +168,24 @@ def test_argument_errors_before_launch():
     dm = _good()
     dm.precision = "mix"
     cm = dm.c()
-    assert lib.rf_sparse_attn(ctypes.byref(cm), a, b2, c3, None, None, None, None, d4, e5,
+    assert lib.rf_sparse_attn(ctypes.byref(cm), a, b2, c3, None, None, None, None, None, d4, e5,
                               info.n_blocks, P(big * 7), None) == 11
-    assert lib.rf_sparse_attn(ctypes.byref(c), a, b2, c3, None, None, None, None, d4, e5,
+    assert lib.rf_sparse_attn(ctypes.byref(c), a, b2, c3, None, None, None, None, None, d4, e5,
                               info.n_blocks, a, None) == 13
-    assert lib.rf_sparse_attn(ctypes.byref(c), a, b2, c3, None, None, None, None, d4, e5,
+    assert lib.rf_sparse_attn(ctypes.byref(c), a, b2, c3, None, None, None, None, None, d4, e5,
                               0, P(big * 7), None) == 4
+    # fp8: every mix buffer but the V scales is not enough; with them the output
+    # may not overlap the scales.
+    f1, f2, f3, f4 = (P(big * i) for i in range(8, 12))
+    assert lib.rf_sparse_attn(ctypes.byref(c8), None, None, c3, f1, f2, f3, f4, None, d4, e5,
+                              info.n_blocks, P(big * 7), None) == 11
+    assert lib.rf_dense_attn(ctypes.byref(c8), None, None, c3, f1, f2, f3, f4, None,
+                             P(big * 7), None) == 11
+    assert lib.rf_dense_attn(ctypes.byref(c8), None, None, c3, f1, f2, f3, f4, P(big * 12),
+                             P(big * 12), None) == 13
     # rf_unpermute: NULL output, aliasing output.
     assert lib.rf_unpermute(ctypes.byref(c), a, None, None) == 1
     assert lib.rf_unpermute(ctypes.byref(c), a, a, None) == 13
     # Nothing to do is not an error: all inputs NULL.
     assert lib.rf_permute(ctypes.byref(c), None, None, None, None, None, None, None, None, None,
-                          None, None, None, None) == 0
+                          None, None, None, None, None) == 0

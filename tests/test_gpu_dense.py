@@ -13,7 +13,8 @@ import pytest
 import oracle
 from synth import WORKLOADS, Workload, make_qkv, to_tnd, from_tnd
 
-from gpu_harness import BF16_TOL, MIX_TOL, assert_close, f32, log, to_dev, to_host_u16
+from gpu_harness import (BF16_TOL, FP8_E2E_TOL, MIX_TOL, assert_close, f32, log, to_dev,
+                         to_host_u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,6 +26,9 @@ def _custom(name, batch, hq, hkv, d, prefix, grid, f0, s, precision="bf16"):
 CASES = {
     "tiny": (WORKLOADS["tiny"], "BNSD"),
     "tiny_mix": (WORKLOADS["tiny"].with_(precision="mix"), "BNSD"),
+    "tiny_fp8": (WORKLOADS["tiny"].with_(precision="fp8"), "BNSD"),
+    "ragged_gqa_fp8": (_custom("ragged_gqa", 1, 4, 2, 128, 200, (10, 17, 34), True, 0.8, "fp8"),
+                       "BNSD"),
     "tiny_tnd_b2": (WORKLOADS["tiny"].with_(batch=2), "TND"),
     "ragged_gqa": (_custom("ragged_gqa", 1, 4, 2, 128, 200, (10, 17, 34), True, 0.8), "BNSD"),
     "minimax_small": (_custom("minimax_small", 1, 2, 2, 128, 512, (6, 24, 42), False, 0.8),
@@ -62,10 +66,11 @@ def test_dense_path_equals_full_attention(name):
     if layout == "TND":
         got = from_tnd(got, w.batch)
     ref = _full_attention(f32(q), f32(k), f32(v), 1.0 / np.sqrt(w.head_dim))
-    assert_close(f32(got), ref, MIX_TOL if w.precision == "mix" else BF16_TOL, f"dense {name}")
+    tol = {"bf16": BF16_TOL, "mix": MIX_TOL, "fp8": FP8_E2E_TOL}[w.precision]
+    assert_close(f32(got), ref, tol, f"dense {name}")
 
 
-@pytest.mark.parametrize("name", ["ragged_gqa", "tiny_mix"])
+@pytest.mark.parametrize("name", ["ragged_gqa", "tiny_mix", "ragged_gqa_fp8"])
 def test_dense_entry_point_equals_sparse_kernel_with_every_block(name):
     import torch
     import block_sparse_video_rf_amd as rf
@@ -79,9 +84,10 @@ def test_dense_entry_point_equals_sparse_kernel_with_every_block(name):
     num = torch.full((rows, w.heads_q), nB, dtype=torch.int32, device="cuda")
     o_sparse = torch.empty_like(b.out_p)
     o_dense = torch.empty_like(b.out_p)
-    rf.rf_sparse_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, idx, num, nB,
-                      o_sparse)
-    rf.rf_dense_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, o_dense)
+    rf.rf_sparse_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, b.v_scale, idx,
+                      num, nB, o_sparse)
+    rf.rf_dense_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, b.v_scale,
+                     o_dense)
     torch.cuda.synchronize()
     assert torch.equal(o_sparse.view(torch.int16), o_dense.view(torch.int16))
 

@@ -15,8 +15,8 @@ import oracle
 from oracle.geometry import plan, permutation
 from synth import WORKLOADS, make_qkv
 
-from gpu_harness import (BF16_TOL, MIX_TOL, assert_close, check_selection, expected_vpt, f32,
-                         geometry_of, log, run_gpu, to_host_u16)
+from gpu_harness import (BF16_TOL, FP8_E2E_TOL, FP8_TOL, MIX_TOL, assert_close, check_selection,
+                         expected_vpt, f32, geometry_of, log, run_gpu, to_host_u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +32,7 @@ def _samples(p, heads, rng, n_sparse=24):
     return sorted(set(picks))
 
 
-@pytest.mark.parametrize("name", ["wan22", "minimax_h3", "wan22_mix", "gqa_long"])
+@pytest.mark.parametrize("name", ["wan22", "minimax_h3", "wan22_mix", "wan22_fp8", "gqa_long"])
 def test_full_size(name):
     import block_sparse_video_rf_amd as rf
     w = WORKLOADS[name]
@@ -51,7 +51,12 @@ def test_full_size(name):
     if bufs.qp is not None:
         assert np.array_equal(to_host_u16(bufs.qp), qp_o)
         assert np.array_equal(to_host_u16(bufs.kp), kp_o)
-    assert np.array_equal(to_host_u16(bufs.vpt), expected_vpt(vp_o, p, w.head_dim))
+    if w.precision == "fp8":
+        v8, sv = oracle.quantize_blocks_pow2(f32(vp_o), p)
+        assert np.array_equal(bufs.vpt.cpu().numpy(), expected_vpt(v8, p, w.head_dim))
+        assert np.array_equal(bufs.v_scale.cpu().numpy(), sv)
+    else:
+        assert np.array_equal(to_host_u16(bufs.vpt), expected_vpt(vp_o, p, w.head_dim))
     log("  permute bit-exact")
     qpool_o = oracle.pool_blocks(f32(qp_o), p)
     kpool_o = oracle.pool_blocks(f32(kp_o), p)
@@ -65,7 +70,7 @@ def test_full_size(name):
     swaps = check_selection(p, w.batch, w.heads_q, gi, gn, scores)
     log(f"  selection exact ({swaps} near-tie rows)")
     q_att, k_att = f32(qp_o), f32(kp_o)
-    if w.precision == "mix":
+    if w.precision in ("mix", "fp8"):
         q8, sq = oracle.quantize_blocks(q_att, p)
         k8, sk = oracle.quantize_blocks(k_att, p)
         assert np.array_equal(bufs.q8.cpu().numpy(), q8)
@@ -84,14 +89,22 @@ def test_full_size(name):
         ids = gi[qb, n, :gn[qb, n]]
         rows = oracle.attention.listed_rows(p, ids)
         refs = []
-        if w.precision == "mix":
+        if w.precision in ("mix", "fp8"):
+            def deq(codes, sig):
+                return np.concatenate([oracle.e4m3_decode(codes[b, n // G, p.blocks[j][0]:
+                                                                p.blocks[j][0] + p.blocks[j][1]])
+                                       * sig[b, n // G, j] for j in ids])
             qd = oracle.e4m3_decode(q8[b, n, r0:r0 + m]) * sq[b, n, qb]
-            kd = np.concatenate([oracle.e4m3_decode(k8[b, n // G, p.blocks[j][0]:
-                                                      p.blocks[j][0] + p.blocks[j][1]])
-                                 * sk[b, n // G, j] for j in ids])
-            refs.append((oracle.attention_block(qd, kd, vp_f[b, n // G, rows], scale), BF16_TOL))
-            refs.append((oracle.attention_block(q_att[b, n, r0:r0 + m], k_att[b, n // G, rows],
-                                                vp_f[b, n // G, rows], scale), MIX_TOL))
+            kd = deq(k8, sk)
+            exact = oracle.attention_block(q_att[b, n, r0:r0 + m], k_att[b, n // G, rows],
+                                           vp_f[b, n // G, rows], scale)
+            if w.precision == "mix":
+                refs.append((oracle.attention_block(qd, kd, vp_f[b, n // G, rows], scale),
+                             BF16_TOL))
+                refs.append((exact, MIX_TOL))
+            else:
+                refs.append((oracle.attention_block_fp8p(qd, kd, deq(v8, sv), scale), FP8_TOL))
+                refs.append((exact, FP8_E2E_TOL))
         else:
             refs.append((oracle.attention_block(q_att[b, n, r0:r0 + m], k_att[b, n // G, rows],
                                                 vp_f[b, n // G, rows], scale), BF16_TOL))

@@ -16,8 +16,8 @@ import oracle
 from oracle.geometry import plan, permutation
 from synth import WORKLOADS, Workload, make_qkv, to_tnd, from_tnd
 
-from gpu_harness import (BF16_TOL, MIX_TOL, assert_close, check_selection, expected_vpt, f32,
-                         geometry_of, log, run_gpu, to_host_u16)
+from gpu_harness import (BF16_TOL, FP8_E2E_TOL, FP8_TOL, MIX_TOL, assert_close, check_selection,
+                         expected_vpt, f32, geometry_of, log, run_gpu, to_host_u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,6 +45,12 @@ SMALL = {
     "sparse_32": (_custom("sparse_32", 1, 2, 2, 64, 128, (3, 8, 256), True, 0.8), {}),
     # sparsity 0 disables sparsity
     "sparsity0": (_custom("sparsity0", 1, 2, 2, 128, 128, (9, 16, 32), True, 0.0), {}),
+    # fp8 precision: D=64, and ragged GQA D=128 in TND with batch 2
+    "tiny_fp8": (WORKLOADS["tiny"].with_(precision="fp8"), {}),
+    "ragged_gqa_fp8": (_custom("ragged_gqa", 1, 4, 2, 128, 200, (10, 17, 34), True, 0.8,
+                               precision="fp8"), {}),
+    "minimax_small_fp8_tnd_b2": (_custom("minimax_small", 2, 2, 2, 128, 512, (6, 24, 42), False,
+                                         0.8, precision="fp8"), {"layout": "TND"}),
     # no geometry at all: dense over a sequence that is not a multiple of 128
     "no_grid": (_custom("no_grid", 1, 2, 2, 128, 1000, (0, 0, 0), False, 0.8), {"grid": (0, 0, 0)}),
 }
@@ -92,19 +98,23 @@ def _full_check(name):
     if bufs.qp is not None:
         assert np.array_equal(to_host_u16(bufs.qp), oracle.permute_rows(qb, pi))
         assert np.array_equal(to_host_u16(bufs.kp), oracle.permute_rows(kb, pi))
-    vpt = to_host_u16(bufs.vpt)
-    assert np.array_equal(vpt, expected_vpt(oracle.permute_rows(vb, pi), p, w.head_dim))
-
     ores = oracle.run(f32(q), f32(k), f32(v), g, precision=w.precision, layout=layout,
                       batch=w.batch)
+    if w.precision == "fp8":
+        vpt = bufs.vpt.cpu().numpy()
+        assert np.array_equal(vpt, expected_vpt(ores["v8"], p, w.head_dim))
+        assert np.array_equal(bufs.v_scale.cpu().numpy(), ores["v_scale"])
+    else:
+        vpt = to_host_u16(bufs.vpt)
+        assert np.array_equal(vpt, expected_vpt(oracle.permute_rows(vb, pi), p, w.head_dim))
     # Step 2: pooled means.
     if not p.fallback:
         qpool = bufs.q_pool.cpu().numpy()
         kpool = bufs.k_pool.cpu().numpy()
         assert np.abs(qpool - ores["q_pool"]).max() <= 2e-6
         assert np.abs(kpool - ores["k_pool"]).max() <= 2e-6
-    # Mix: codes and scales, bit for bit.
-    if w.precision == "mix":
+    # Mix and fp8: codes and scales, bit for bit.
+    if w.precision in ("mix", "fp8"):
         assert np.array_equal(bufs.q8.cpu().numpy(), ores["q8"])
         assert np.array_equal(bufs.k8.cpu().numpy(), ores["k8"])
         assert np.array_equal(bufs.q_scale.cpu().numpy(), ores["q_scale"])
@@ -118,8 +128,9 @@ def _full_check(name):
     out = f32(to_host_u16(res["out"]))
     ref_same_sel = oracle.run(f32(q), f32(k), f32(v), g, precision=w.precision, layout=layout,
                               batch=w.batch, select=(gi, gn))["out"]
-    assert_close(out, ref_same_sel, BF16_TOL, "attention (GPU lists)")
-    tol = MIX_TOL if w.precision == "mix" else BF16_TOL
+    assert_close(out, ref_same_sel, FP8_TOL if w.precision == "fp8" else BF16_TOL,
+                 "attention (GPU lists)")
+    tol = {"bf16": BF16_TOL, "mix": MIX_TOL, "fp8": FP8_E2E_TOL}[w.precision]
     bf16_ref = ores["out"] if w.precision == "bf16" else oracle.run(
         f32(q), f32(k), f32(v), g, layout=layout, batch=w.batch)["out"]
     assert_close(out, bf16_ref, tol, "end to end vs bf16 oracle")
@@ -192,7 +203,7 @@ def test_handmade_lists_skip_invalid_entries():
             valid_num[qb, n] = len(good)
     num = np.minimum(num, nB)
     out_p = torch.empty_like(b.out_p)
-    rf.rf_sparse_attn(desc, b.qp, b.kp, b.vpt, None, None, None, None,
+    rf.rf_sparse_attn(desc, b.qp, b.kp, b.vpt, None, None, None, None, None,
                       torch.from_numpy(idx).cuda(), torch.from_numpy(num).cuda(), nB, out_p)
     torch.cuda.synchronize()
     g = geometry_of(desc)

@@ -24,7 +24,7 @@ def dump_exe(tmp_path_factory):
         f.write('#include "rf_internal.h"\n'
                 'rf_status rf_launch_permute(const RfGeom&, int32_t, const void*, const void*, '
                 'const void*, void*, void*, void*, float*, float*, uint8_t*, uint8_t*, float*, '
-                'float*, void*) { return RF_ERR_HIP; }\n'
+                'float*, float*, void*) { return RF_ERR_HIP; }\n'
                 'rf_status rf_launch_unpermute(const RfGeom&, const void*, void*, void*) '
                 '{ return RF_ERR_HIP; }\n'
                 'rf_status rf_launch_pool_select(const RfGeom&, float, const void*, const void*, '
@@ -32,7 +32,8 @@ def dump_exe(tmp_path_factory):
                 '{ return RF_ERR_HIP; }\n'
                 'rf_status rf_launch_sparse_attn(const RfGeom&, int32_t, float, const void*, '
                 'const void*, const void*, const uint8_t*, const uint8_t*, const float*, '
-                'const float*, const int32_t*, const int32_t*, int32_t, void*, void*) '
+                'const float*, const float*, const int32_t*, const int32_t*, int32_t, void*, '
+                'void*) '
                 '{ return RF_ERR_HIP; }\n')
     subprocess.run(["g++", "-O1", "-std=c++17", "-fsanitize=address,undefined",
                     "-I", os.path.join(ROOT, "include"),

@@ -69,11 +69,17 @@ __device__ __forceinline__ int kappa(int r) {
 }
 
 // Key row order for fp8 O^T products: A-operand row i of key tile t holds key
-// 16 t + kappa8(i) of the wave's 64, which puts keys 32 (l / 32) + [0, 32) in
-// lane l's two accumulator tiles (tile t, value v = key 32 (l / 32) + 16 t + v):
-// exactly the 32-byte k-slice of the fp8 B operand, in order.
-__device__ __forceinline__ int kappa8(int r) {
-  return (r & 3) | ((r >> 3) << 2) | (((r >> 2) & 1) << 5);
+// 16 t + kappa8(i) of the wave's 64, kappa8(i) = (i & 3) + 4 (i >> 3) +
+// 32 ((i >> 2) & 1), which puts keys 32 (l / 32) + [0, 32) in lane l's two
+// accumulator tiles (tile t, value v = key 32 (l / 32) + 16 t + v): exactly the
+// 32-byte k-slice of the fp8 B operand, in order. Reading rows kappa8(i)
+// directly would put rows r and r + 32 in one 16-lane read (the same banks for
+// any 16-byte-aligned stride), so the K tile is stored in that order instead:
+// key r of the 128-row block goes to LDS row kslot8(r), and lane i of key tile
+// t reads row 64 kh + 32 t + i.
+__device__ __forceinline__ int kslot8(int r) {
+  return (r & 64) | (((r >> 4) & 1) << 5) | (((r >> 2) & 3) << 3) | (((r >> 5) & 1) << 2) |
+         (r & 3);
 }
 
 // The hardware hands workgroup i to XCD i % 8 (MI355X has 8 XCDs, each with
@@ -137,6 +143,20 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Workgroup barrier after which this wave's LDS stores are visible, while its
+// last N LDS operations (reads) may still be in flight: LDS operations of a
+// wave complete in issue order, so at most N outstanding means every earlier
+// one (the stores) is done. Scalar loads count too, which only makes the wait
+// stricter. The caller keeps those N reads last (a scheduling fence before
+// them).
+template <int N>
+__device__ __forceinline__ void lds_barrier_keep() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Maxima without the NaN canonicalisation fmaxf needs (no NaN reaches them:
 // masked scores are -inf).
 __device__ __forceinline__ float max3f(float a, float b, float c) {
@@ -176,11 +196,15 @@ struct MfmaPlan {
   static constexpr int NPV = V8 ? DT : 4 * DT;
   static constexpr int PV_RPM = V8 ? 2 : 1;          // reads per O^T product
   static constexpr int NREAD = NS_READ + NPV * PV_RPM;
-  static constexpr int NMFMA = NS_MFMA + NPV;
+  // fp8: one more product, of an all-ones A operand with P^T, accumulates the
+  // row sums of the rounded P (no LDS reads).
+  static constexpr int NSUM = V8 ? 1 : 0;
+  static constexpr int NMFMA = NS_MFMA + NPV + NSUM;
   static constexpr int NR = 8;                       // fragments in flight
   static constexpr int NPRE = NR < NS_READ ? NR : NS_READ;  // K reads issued before the barrier
   static constexpr int rend(int m) {
-    return m < NS_MFMA ? (m + 1) * S_RPM : NS_READ + (m - NS_MFMA + 1) * PV_RPM;
+    return m < NS_MFMA ? (m + 1) * S_RPM
+                       : (m < NS_MFMA + NPV ? NS_READ + (m - NS_MFMA + 1) * PV_RPM : NREAD);
   }
 };
 
@@ -214,6 +238,7 @@ struct MfmaCtx {
   bf16x8 pf16[2][2];              // P^T operands, bf16 O^T products
   i32x8 pf8;                      // P^T operand (E4M3 codes), fp8 O^T products
   int vexp;                       // E8M0 scale of the previous block's V (fp8)
+  f32x16 osum;                    // fp8: every value is the running row sum of P
 };
 
 // Bytes per row of a K tile and of a V^T tile in global memory, and their
@@ -233,11 +258,9 @@ __device__ __forceinline__ const uint8_t* read_addr(const MfmaCtx<D, PREC>& c) {
   using P = MfmaPlan<D, PREC>;
   using TG = TileGeom<D, PREC>;
   if constexpr (R < P::NS_READ) {
-    // S^T product sm: key tile t (rows 32 t, or 16 t for the fp8 row order),
-    // channel k-step st.
+    // S^T product sm: key tile t (LDS rows 32 t + [0, 32)), channel k-step st.
     constexpr int sm = R / P::S_RPM, half = R % P::S_RPM, st = sm / 2, t = sm % 2;
-    constexpr int trow = P::V8 ? 16 : 32;
-    return c.kbase + trow * t * TG::KSTR + (P::QK8 ? 64 * st + 16 * half : 32 * st);
+    return c.kbase + 32 * t * TG::KSTR + (P::QK8 ? 64 * st + 16 * half : 32 * st);
   } else if constexpr (P::V8) {
     // O^T product e (channel tile): 32 key bytes of V^T row 32 e + li.
     constexpr int pr = R - P::NS_READ, e = pr / 2, half = pr % 2;
@@ -255,6 +278,29 @@ __device__ __forceinline__ void issue_reads(MfmaCtx<D, PREC>& c) {
     ring_slot<R % P::NR>(c.ring) = *reinterpret_cast<const uint4*>(read_addr<D, PREC, R>(c));
     issue_reads<D, PREC, R + 1, END>(c);
   }
+}
+
+// Keeps every product of an MFMA interval inside it. The scaled fp8 product
+// intrinsic can be sunk by the compiler's IR passes (sched_barrier only binds
+// the machine scheduler) into the next interval, next to the first use of its
+// result, which would serialise it with the softmax. An empty asm statement
+// that takes the accumulators as inputs must follow their products. (The host
+// pass of the compiler parses device code too and has no VGPR tuples: the
+// statements exist for the device pass only.)
+__device__ __forceinline__ void pin_acc(const f32x16& x) {
+#if __HIP_DEVICE_COMPILE__
+  asm volatile("" ::"v"(x));
+#else
+  (void)x;
+#endif
+}
+template <int D, int PREC>
+__device__ __forceinline__ void pin_products(MfmaCtx<D, PREC>& c) {
+  pin_acc(c.s[0]);
+  pin_acc(c.s[1]);
+#pragma unroll
+  for (int e = 0; e < MfmaPlan<D, PREC>::DT; ++e) pin_acc(c.o[e]);
+  if constexpr (Prec<PREC>::V8) pin_acc(c.osum);
 }
 
 template <int NR, int R>
@@ -278,6 +324,13 @@ __device__ __forceinline__ void mfma_steps(MfmaCtx<D, PREC>& c) {
         __builtin_memcpy(&ka, &ring_slot<M % P::NR>(c.ring), 16);
         c.s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, c.qf[st], c.s[t], 0, 0, 0);
       }
+    } else if constexpr (P::V8 && M == P::NMFMA - 1) {
+      // Row sums: (all-ones 32 x 64) x P^T puts the sum of this lane's query row
+      // over the wave's 64 keys in every accumulator value (E4M3 1.0 = 0x38).
+      constexpr int k1 = 0x38383838;
+      const i32x8 ones = {k1, k1, k1, k1, k1, k1, k1, k1};
+      c.osum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, c.pf8, c.osum, 0, 0, 0, 127,
+                                                               0, 127);
     } else if constexpr (P::V8) {
       // O^T tile e += 2^(vexp - 127) V^T (E4M3) P^T (E4M3) over the wave's 64 keys.
       constexpr int e = M - P::NS_MFMA;
@@ -290,6 +343,12 @@ __device__ __forceinline__ void mfma_steps(MfmaCtx<D, PREC>& c) {
       bf16x8 va;
       __builtin_memcpy(&va, &ring_slot<r % P::NR>(c.ring), 16);
       c.o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, c.pf16[tu / 2][tu % 2], c.o[e], 0, 0, 0);
+    }
+    // fp8 S^T products stay first (see pin_products): their results are
+    // pinned one product later, so the pin itself waits for nothing.
+    if constexpr (P::QK8 && M == P::NS_MFMA) {
+      pin_acc(c.s[0]);
+      pin_acc(c.s[1]);
     }
     // Refill the slots this product consumed: NR reads stay ahead.
     constexpr int done_before = M == 0 ? 0 : P::rend(M - 1);
@@ -406,6 +465,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) c.pf16[t][u] = bf16x8{};
   c.pf8 = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  c.osum = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int64_t sel_row = ((int64_t)b * g.n_blocks + q) * g.N1 + n;
@@ -444,7 +504,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
 #define RF_KST1(BUF, VAR, M)                                                               \
   if constexpr ((M) < K_CH) {                                                              \
     const int slot_ = (M) * 256 + gt, r_ = slot_ / KCH, c_ = slot_ % KCH;                  \
-    *reinterpret_cast<u32x4*>((BUF) + r_ * KSTR + c_ * 16) = VAR;                          \
+    *reinterpret_cast<u32x4*>((BUF) + (V8 ? kslot8(r_) : r_) * KSTR + c_ * 16) = VAR;      \
   }
 #define RF_VST1(BUF, VAR, M)                                                               \
   if constexpr ((M) < V_CH) {                                                              \
@@ -501,10 +561,10 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   lds_barrier();
   if (kh == 1) lds_barrier();  // the kh = 1 group runs one interval behind
 
-  // This lane's fragment bases: K row 64 kh + kappa(li) (+ 32 t) (fp8:
-  // kappa8(li) (+ 16 t)), V^T row li (+ 32 e) at key column 64 kh + 8 h
-  // (+ 16 k-step) (fp8: 64 kh + 32 h).
-  const int krow = V8 ? kappa8(li) : kappa(li);
+  // This lane's fragment bases: K row 64 kh + kappa(li) (+ 32 t) (fp8: LDS row
+  // 64 kh + li (+ 32 t), holding key 64 kh + 16 t + kappa8(li)), V^T row li
+  // (+ 32 e) at key column 64 kh + 8 h (+ 16 k-step) (fp8: 64 kh + 32 h).
+  const int krow = V8 ? li : kappa(li);
   const int koff = (64 * kh + krow) * KSTR + (MIX ? 32 * h : 16 * h);
   const int voff = V8 ? li * VSTR + 64 * kh + 32 * h : li * VSTR + 2 * (64 * kh + 8 * h);
   c.vexp = 127;
@@ -551,6 +611,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
       RF_GLD1(st7, 7)
 #undef RF_Q
     }
+    pin_products(c);
     lds_barrier();
 
     // ---- VALU interval ----
@@ -609,6 +670,10 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
       for (int e = 0; e < DT; ++e)
 #pragma unroll
         for (int v = 0; v < 16; ++v) c.o[e][v] *= alpha;
+      if constexpr (V8) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) c.osum[v] *= alpha;
+      }
     }
     // While every key so far is masked m_run is -inf; any finite stand-in keeps
     // exp2(-inf - m) at 0 instead of NaN.
@@ -617,8 +682,8 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     float lsum = 0.0f;
     if constexpr (V8) {
       // P as E4M3 codes (round to nearest even; P <= 2^8 < 448), byte 16 t + v
-      // of the B operand; the row sum adds the rounded values (they are what
-      // multiplies V).
+      // of the B operand. The row sum of the rounded values (what multiplies
+      // V) comes from the all-ones product in the next MFMA interval.
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const int t = w / 4, v0 = 4 * (w % 4);
@@ -628,9 +693,6 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
         int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
         pk = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], pk, true);
         c.pf8[w] = pk;
-        const auto r0 = __builtin_amdgcn_cvt_pk_f32_fp8(pk, false);
-        const auto r1 = __builtin_amdgcn_cvt_pk_f32_fp8(pk, true);
-        lsum += (r0[0] + r0[1]) + (r1[0] + r1[1]);
       }
       c.vexp = (int)((__float_as_uint(vscale[j]) >> 23) & 0xffu);
     } else {
@@ -647,11 +709,14 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     }
     l_run += lsum;
 
-    // First K fragments of block i + 1 (written at least one interval ago).
+    // First K fragments of block i + 1 (written at least one interval ago,
+    // overwritten no earlier than two intervals on): they stay in flight across
+    // the barrier, which waits only for this wave's tile stores.
     par ^= 1;
     c.kbase = kbuf0 + par * KT + koff;
+    __builtin_amdgcn_sched_barrier(0);
     issue_reads<D, PREC, 0, PL::NPRE>(c);
-    lds_barrier();
+    lds_barrier_keep<PL::NPRE>();
     w0 = w1;
     w1 = w2;
     w2 = w3;
@@ -670,6 +735,10 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
         c.o[e] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, c.pf8, c.o[e], 0, 0, 0, c.vexp,
                                                                  0, 127);
       }
+      constexpr int k1 = 0x38383838;
+      const i32x8 ones = {k1, k1, k1, k1, k1, k1, k1, k1};
+      c.osum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, c.pf8, c.osum, 0, 0, 0, 127,
+                                                               0, 127);
     } else {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -684,6 +753,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     }
   }
   if (kh == 0) lds_barrier();  // matches the kh = 1 group's extra barrier
+  if constexpr (V8) l_run = c.osum[0];  // the row sum over this wave's keys (any value)
 
 #undef RF_LOAD_K
 #undef RF_STORE_K
@@ -712,7 +782,10 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   const float a0 = mm == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mm);
   const float a1 = mm == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - mm);
   float lt = l_run * a0 + l1 * a1;
-  lt += __shfl_xor(lt, 32);
+  // bf16 and mix: each lane summed the keys of its own half-wave, so the row
+  // sum adds the partner lane's. fp8: the all-ones product already gave every
+  // lane the sum over all the wave's keys.
+  if constexpr (!V8) lt += __shfl_xor(lt, 32);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (qvalid) {
     uint16_t* orow = a.out_p + (((int64_t)b * g.N1 + n) * g.S + row0 + qrow) * D;

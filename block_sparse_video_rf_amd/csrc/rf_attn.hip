@@ -324,7 +324,7 @@ __device__ __forceinline__ void mfma_steps(MfmaCtx<D, PREC>& c) {
         __builtin_memcpy(&ka, &ring_slot<M % P::NR>(c.ring), 16);
         c.s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, c.qf[st], c.s[t], 0, 0, 0);
       }
-    } else if constexpr (P::V8 && M == P::NMFMA - 1) {
+    } else if constexpr (P::V8 && M == P::NS_MFMA + P::NPV) {
       // Row sums: (all-ones 32 x 64) x P^T puts the sum of this lane's query row
       // over the wave's 64 keys in every accumulator value (E4M3 1.0 = 0x38).
       constexpr int k1 = 0x38383838;

@@ -62,6 +62,17 @@ __device__ __forceinline__ uint32_t e4m3_rne(float y) {
   return sign | (e << 3) | ((r >> 20) & 7u);
 }
 
+// Streaming (non-temporal) stores of 16 and 8 bytes: outputs that this kernel
+// does not read again.
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_stream(void* p, uint32_t x, uint32_t y, uint32_t z, uint32_t w) {
+  __builtin_nontemporal_store(v4u{x, y, z, w}, reinterpret_cast<v4u*>(p));
+}
+__device__ __forceinline__ void store_stream(void* p, uint32_t x, uint32_t y) {
+  __builtin_nontemporal_store(v2u{x, y}, reinterpret_cast<v2u*>(p));
+}
+
 // Smallest e with amax <= 448 * 2^e, clamped to [-126, 127] (a normal fp32
 // power of two); 0 for amax == 0. With amax = f * 2^x, f in [0.5, 1), and
 // 448 = 0.875 * 2^9: e = x - 9 if f <= 0.875, else x - 8 (exact).
@@ -178,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
           }
           w[e] = x;
         }
-        *reinterpret_cast<uint4*>(dst + d * 128 + cc * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+        store_stream(dst + d * 128 + cc * 16, w[0], w[1], w[2], w[3]);
       }
       if (tid == 0) a.v_scale[((int64_t)b * g.N2 + n) * g.n_blocks + j] = ldexpf(1.0f, ex);
       return;
@@ -202,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
         const uint32_t hi = tile[(cc * 8 + 2 * e + 1) * (D + 8) + d];
         w[e] = lo | (hi << 16);
       }
-      *reinterpret_cast<uint4*>(dst + d * 128 + cc * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+      store_stream(dst + d * 128 + cc * 8, w[0], w[1], w[2], w[3]);
     }
     return;
   }
@@ -214,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int i = p * RPP + rsub;
-      if (i < len) *reinterpret_cast<uint4*>(dstp + base + (int64_t)i * D + c * 8) = val[p];
+      if (i < len) store_stream(dstp + base + (int64_t)i * D + c * 8, val[p].x, val[p].y, val[p].z, val[p].w);
     }
   }
 
@@ -272,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
           hi |= e4m3_rne(bf_lo(w[e + 2]) * r) << (16 * e);
           hi |= e4m3_rne(bf_hi(w[e + 2]) * r) << (16 * e + 8);
         }
-        *reinterpret_cast<uint2*>(q8 + base + (int64_t)i * D + c * 8) = make_uint2(lo, hi);
+        store_stream(q8 + base + (int64_t)i * D + c * 8, lo, hi);
       }
     }
     float* sc = kind == 0 ? a.q_scale : a.k_scale;
@@ -311,8 +322,8 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(UnpermuteArgs a) {
     const int i = p * RPP + rsub;
     if (i < len) {
       const int64_t nat = rf_natural_row(g, row0 + i);
-      *reinterpret_cast<uint4*>(a.out + rf_row_offset(g, g.layout, g.N1, b, n, nat) + c * 8) =
-          val[p];
+      store_stream(a.out + rf_row_offset(g, g.layout, g.N1, b, n, nat) + c * 8, val[p].x, val[p].y,
+                   val[p].z, val[p].w);
     }
   }
 }

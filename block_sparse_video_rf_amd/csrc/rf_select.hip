@@ -13,13 +13,18 @@
 //   score_kernel  per (batch, query head): Sc = scale * Qbar Kbar^T over the
 //                 sparse blocks, a small fp32 GEMM tiled 64x64 through LDS
 //                 (4x4 outputs per thread, fixed summation order over D).
-//   select_kernel one workgroup per selectIdx row (batch, query block, head):
-//                 dense query blocks write 0..n_blocks-1; sparse ones find the
-//                 k-th largest score with a 4-pass 8-bit radix select over
-//                 order-preserving keys held in LDS, keep every key above it
-//                 and the lowest-id keys equal to it, and write the ascending
-//                 union with the dense blocks. Integer work only after the
-//                 scores, so the list is exact for given scores.
+//   select_wave_kernel  one wave per selectIdx row (batch, query block, head),
+//                 up to 2048 sparse blocks: dense query blocks write
+//                 0..n_blocks-1; sparse ones hold the row's order-preserving
+//                 score keys in registers, build the k-th largest key bit by
+//                 bit from the top (a bit stays set while at least k keys are
+//                 >= the candidate, counted with ballots), keep every key above
+//                 it and the lowest-id keys equal to it, and write the
+//                 ascending union with the dense blocks.
+//   select_kernel the same rule with one workgroup per row and the keys in LDS
+//                 (a 4-pass 8-bit radix select), for more sparse blocks.
+//   Integer work only after the scores, so the lists are exact for given
+//   scores, and both kernels give the same lists.
 #include <hip/hip_runtime.h>
 
 #include "rf_internal.h"
@@ -167,6 +172,97 @@ __device__ __forceinline__ int block_inclusive_scan(int x, int* buf) {
   return r;
 }
 
+// Exclusive prefix sum of one int per lane over a wave.
+__device__ __forceinline__ int wave_exclusive_scan(int x, int lane) {
+  int incl = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  return incl - x;
+}
+
+// One wave per selectIdx row; lane l holds the keys of sparse ids
+// [PER l, PER l + PER), so id order is lane-major and then slot order.
+template <int PER>
+__global__ __launch_bounds__(kThreads) void select_wave_kernel(SelectArgs a) {
+  const RfGeom& g = a.g;
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = (int64_t)g.B * g.N1 * g.n_blocks;
+  // Rows ordered (batch, head, query block), query block fastest: the waves of
+  // a workgroup read neighbouring score rows.
+  const int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (r >= rows) return;  // uniform over the wave
+  const int32_t q = (int32_t)(r % g.n_blocks);
+  const int64_t bn = r / g.n_blocks;
+  const int32_t n = (int32_t)(bn % g.N1), b = (int32_t)(bn / g.N1);
+  const int64_t row = (int64_t)b * g.n_blocks + q;
+  int32_t* out = a.select_idx + (row * g.N1 + n) * a.max_kv;
+  const int32_t nB = g.n_blocks;
+  const bool sparse_q = q >= g.n_head && q < g.n_head + g.n_sparse;
+  if (!sparse_q) {
+    for (int p = lane; p < a.max_kv; p += 64) out[p] = p < nB ? p : -1;
+    if (lane == 0) a.select_num[row * g.N1 + n] = nB;
+    return;
+  }
+  const int nS = g.n_sparse, k = g.topk;
+  const int32_t nh = g.n_head;
+  const int count = nh + k + g.n_tail;
+  for (int p = lane; p < a.max_kv; p += 64) {
+    if (p < nh) out[p] = p;
+    else if (p >= nh + k && p < count) out[p] = nh + nS + (p - nh - k);
+    else if (p >= count) out[p] = -1;
+  }
+  if (lane == 0) a.select_num[row * g.N1 + n] = count;
+  if (k == 0) return;
+
+  const float* sc = a.scores + (((int64_t)b * g.N1 + n) * nS + (q - nh)) * nS;
+  const int i0 = lane * PER;
+  uint32_t key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) key[i] = i0 + i < nS ? order_key(sc[i0 + i]) : 0u;
+  // Finite scores have keys > 0, so the zero keys of unused slots never reach
+  // the threshold.
+  uint32_t kth = 0;
+  int need = k;  // keys equal to kth still to take (lowest ids first)
+  if (k < nS) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = kth | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+      if (cnt >= k) kth = cand;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) gt += __popcll(__ballot(key[i] > kth));
+    need = k - gt;
+  }
+  int eq = 0;
+  if (k < nS) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) eq += (i0 + i < nS && key[i] == kth) ? 1 : 0;
+  }
+  int rank = wave_exclusive_scan(eq, lane);  // ties with lower ids
+  bool take[PER];
+  int ntake = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    bool t;
+    if (i0 + i >= nS) t = false;
+    else if (k >= nS || key[i] > kth) t = true;
+    else if (key[i] == kth) t = rank++ < need;
+    else t = false;
+    take[i] = t;
+    ntake += t ? 1 : 0;
+  }
+  int pos = nh + wave_exclusive_scan(ntake, lane);
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (take[i]) out[pos++] = nh + i0 + i;
+}
+
 __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
   __shared__ uint32_t keys[RF_MAX_SPARSE_BLOCKS];
   __shared__ int hist[kThreads];
@@ -309,6 +405,15 @@ rf_status rf_launch_pool_select(const RfGeom& g, float scale, const void* qp, co
     hipLaunchKernelGGL(score_kernel, dim3(tiles, tiles, g.B * g.N1), dim3(kThreads), 0, s, ca);
     sa.scores = scores;
   }
-  hipLaunchKernelGGL(select_kernel, dim3(g.n_blocks, g.N1, g.B), dim3(kThreads), 0, s, sa);
+  const int64_t rows = (int64_t)g.B * g.N1 * g.n_blocks;
+  const dim3 wave_grid((uint32_t)((rows + kThreads / 64 - 1) / (kThreads / 64)));
+  if (g.n_sparse <= 512)
+    hipLaunchKernelGGL(select_wave_kernel<8>, wave_grid, dim3(kThreads), 0, s, sa);
+  else if (g.n_sparse <= 1024)
+    hipLaunchKernelGGL(select_wave_kernel<16>, wave_grid, dim3(kThreads), 0, s, sa);
+  else if (g.n_sparse <= 2048)
+    hipLaunchKernelGGL(select_wave_kernel<32>, wave_grid, dim3(kThreads), 0, s, sa);
+  else
+    hipLaunchKernelGGL(select_kernel, dim3(g.n_blocks, g.N1, g.B), dim3(kThreads), 0, s, sa);
   return hipGetLastError() == hipSuccess ? RF_OK : RF_ERR_HIP;
 }

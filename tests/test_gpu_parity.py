@@ -232,3 +232,31 @@ def test_recomputed_pools_and_determinism():
     rf.rf_pool_select(desc, b.qp, b.kp, None, None, idx2, num2, b.info.n_blocks, b.workspace)
     torch.cuda.synchronize()
     assert torch.equal(idx2, b.select_idx) and torch.equal(num2, b.select_num)
+
+
+@pytest.mark.parametrize("grid", [(5, 16, 1200), (3, 16, 8400)], ids=["nS600", "nS2100"])
+def test_selection_paths_by_sparse_count(grid):
+    """Selection alone at 600 sparse blocks (16 keys per lane) and at 2100 (above
+    the register path: one workgroup per row), against the oracle's rule."""
+    import torch
+    import block_sparse_video_rf_amd as rf
+    w = _custom("sel", 1, 1, 1, 64, 128, grid, True, 0.8)
+    desc = rf.Desc.from_workload(w)
+    log(f"[selection nS] grid={grid} S={w.seq_len}")
+    q, k, v = make_qkv(w)
+    b = rf.Buffers(desc)
+    rf.rf_permute(desc, *(torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(
+        torch.bfloat16).cuda() for x in (q, k, v)), b.qp, b.kp, b.vpt, b.q_pool, b.k_pool)
+    rf.rf_pool_select(desc, b.qp, b.kp, b.q_pool, b.k_pool, b.select_idx, b.select_num,
+                      b.info.n_blocks, b.workspace)
+    torch.cuda.synchronize()
+    g = geometry_of(desc)
+    p = plan(g)
+    assert p.n_sparse == b.info.n_sparse == grid[1] // 8 * grid[2] // 8 * ((grid[0] - 1) // 2)
+    pi = permutation(g)
+    qpool = oracle.pool_blocks(f32(oracle.permute_rows(q, pi)), p)
+    kpool = oracle.pool_blocks(f32(oracle.permute_rows(k, pi)), p)
+    scores = oracle.block_scores(qpool, kpool, 1.0 / np.sqrt(w.head_dim))
+    swaps = check_selection(p, 1, 1, b.select_idx.cpu().numpy(), b.select_num.cpu().numpy(),
+                            scores)
+    log(f"  selection exact ({swaps} near-tie rows)")

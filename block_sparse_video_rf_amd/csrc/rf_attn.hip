@@ -642,28 +642,19 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     float cs = a.scale_log2;
     if constexpr (MIX) cs *= q_sigma * kscale[j];
 
-    // Maximum over this wave's keys of the row (then the partner half-wave).
-    float m0 = c.s[0][0], m1 = c.s[1][0];
+    // Row maximum over this wave's keys (then the partner half-wave), times cs.
+    auto block_max = [&]() -> float {
+      float m0 = c.s[0][0], m1 = c.s[1][0];
 #pragma unroll
-    for (int v = 1; v < 15; v += 2) {
-      m0 = max3f(m0, c.s[0][v], c.s[0][v + 1]);
-      m1 = max3f(m1, c.s[1][v], c.s[1][v + 1]);
-    }
-    const float mx = max_halves(max3f(m0, m1, max3f(c.s[0][15], c.s[1][15], c.s[1][15])));
-    // The reference maximum m_run only moves when the block exceeds it by more
-    // than 8 (log2 units): exponentials stay <= 2^8, which bf16 P and fp32 sums
-    // hold as well, and the rescale of O is skipped for most blocks. O^T holds
-    // every product up to the previous block here, exactly what the rescale
-    // must cover.
-    // fp8: P = 2^(t - m_run + 8) goes to E4M3 (largest finite 448), so m_run is
-    // the integer ceiling of the running maximum, raised as soon as a block
-    // exceeds it: the largest P stays in (128, 256], and the rescale by a
-    // power of two is exact and leaves the rounding of normal P unchanged.
-    const float mc = mx * cs;
-    if (__any(mc > m_run + (V8 ? 0.0f : 8.0f))) {
-      const float m_new = fmaxf(m_run, V8 ? ceilf(mc) : mc);
-      const float alpha = V8 ? (m_run == -INFINITY ? 0.0f : ldexpf(1.0f, (int)(m_run - m_new)))
-                             : __builtin_amdgcn_exp2f(m_run - m_new);
+      for (int v = 1; v < 15; v += 2) {
+        m0 = max3f(m0, c.s[0][v], c.s[0][v + 1]);
+        m1 = max3f(m1, c.s[1][v], c.s[1][v + 1]);
+      }
+      return max_halves(max3f(m0, m1, max3f(c.s[0][15], c.s[1][15], c.s[1][15]))) * cs;
+    };
+    // O^T holds every product up to the previous block here, exactly what a
+    // rescale of the running state must cover.
+    auto rescale = [&](float m_new, float alpha) {
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -674,13 +665,23 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) c.osum[v] *= alpha;
       }
-    }
+    };
     // While every key so far is masked m_run is -inf; any finite stand-in keeps
     // exp2(-inf - m) at 0 instead of NaN.
-    const float mneg = (V8 ? 8.0f : 0.0f) - fmaxf(m_run, -1e30f);
+    auto ref_neg = [&]() -> float { return (V8 ? 8.0f : 0.0f) - fmaxf(m_run, -1e30f); };
 
     float lsum = 0.0f;
     if constexpr (V8) {
+      // fp8: P = 2^(t - m_run + 8) goes to E4M3 (largest finite 448), so m_run
+      // is the integer ceiling of the running maximum, raised as soon as a
+      // block exceeds it: the largest P stays in (128, 256], and the rescale by
+      // a power of two is exact and leaves the rounding of normal P unchanged.
+      const float mc = block_max();
+      if (__any(mc > m_run)) {
+        const float m_new = fmaxf(m_run, ceilf(mc));
+        rescale(m_new, m_run == -INFINITY ? 0.0f : ldexpf(1.0f, (int)(m_run - m_new)));
+      }
+      const float mneg = ref_neg();
       // P as E4M3 codes (round to nearest even; P <= 2^8 < 448), byte 16 t + v
       // of the B operand. The row sum of the rounded values (what multiplies
       // V) comes from the all-ones product in the next MFMA interval.
@@ -696,16 +697,32 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
       }
       c.vexp = (int)((__float_as_uint(vscale[j]) >> 23) & 0xffu);
     } else {
+      // bf16 P and fp32 sums hold exponentials far beyond 1, so the reference
+      // m_run is only a guard against overflow: the exponentials are taken
+      // against the current one, and only if some row's block sum leaves
+      // (0, 2^64] (or no key has been seen yet, m_run = -inf) is the block
+      // maximum computed, m_run raised to it and the block redone.
+      auto exps = [&](float mneg) -> float {
+        float ls = 0.0f;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+          for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(c.s[t][8 * u + m], cs, mneg));
-            lsum += p;
-            c.pf16[t][u][m] = (__bf16)p;
-          }
+            for (int m = 0; m < 8; ++m) {
+              const float p = __builtin_amdgcn_exp2f(fmaf(c.s[t][8 * u + m], cs, mneg));
+              ls += p;
+              c.pf16[t][u][m] = (__bf16)p;
+            }
+        return ls;
+      };
+      lsum = exps(ref_neg());
+      if (__any(!(lsum <= 0x1p64f))) {
+        const float m_new = fmaxf(m_run, block_max());
+        // (m_run = -inf: nothing accumulated yet; alpha 0 also when m_new stays -inf.)
+        rescale(m_new, m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new));
+        lsum = exps(ref_neg());
+      }
     }
     l_run += lsum;
 

@@ -12,9 +12,15 @@ Comparison rules:
 * pooled means: |gpu - oracle| <= 2e-6 (fp32 sums of 128 bf16 values);
 * attention output: max-abs <= 2e-2 and mean-abs <= 2e-3 against the float64
   oracle (bf16), 6e-2 / 6e-3 for the mix precision;
-* fp8 precision: 2e-2 / 2e-3 against the oracle's fp8 reading on the same
+* fp8 precision: 6e-2 / 2e-3 against the oracle's fp8 reading on the same
   codes (FP8_TOL), 1.2e-1 / 1.2e-2 against the unquantised oracle
   (FP8_E2E_TOL: the mix bound doubled, for V and P rounded to E4M3 as well).
+  FP8_TOL: the kernel takes logits and exponentials in fp32, the oracle in
+  float64, so an exponential that lies within fp32 rounding of an E4M3
+  rounding midpoint can round to the neighbouring code on one side: one ulp,
+  1/8 of that P. A P that carries a share w of its row then moves the output
+  by at most w/8 * max|v - O|; the max bound allows w up to about 0.1 with
+  |v| up to 4 (short rows of few keys), the mean bound is unchanged.
 """
 from __future__ import annotations
 
@@ -29,7 +35,7 @@ from synth import bf16_to_f32
 
 BF16_TOL = (2e-2, 2e-3)
 MIX_TOL = (6e-2, 6e-3)
-FP8_TOL = (2e-2, 2e-3)
+FP8_TOL = (6e-2, 2e-3)
 FP8_E2E_TOL = (1.2e-1, 1.2e-2)
 NEAR_TIE_REL = 1e-5
 

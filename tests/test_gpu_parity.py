@@ -164,9 +164,10 @@ def test_dense_cases_equal_dense_attention():
         assert_close(f32(to_host_u16(res["out"])), ref, BF16_TOL, f"{name} vs torch SDPA")
 
 
-def test_empty_lists_give_zeros():
+@pytest.mark.parametrize("precision", ["bf16", "mix", "fp8"])
+def test_empty_lists_give_zeros(precision):
     """Sparsity 1, no prefix, no first frame, aligned grid: every list is empty."""
-    w = _custom("empty", 1, 2, 2, 128, 0, (4, 16, 16), False, 1.0)
+    w = _custom("empty", 1, 2, 2, 128, 0, (4, 16, 16), False, 1.0, precision=precision)
     import block_sparse_video_rf_amd as rf
     desc = rf.Desc.from_workload(w, min_sparse_blocks=1)
     q, k, v = make_qkv(w)
@@ -175,11 +176,12 @@ def test_empty_lists_give_zeros():
     assert np.all(to_host_u16(res["out"]) == 0)
 
 
-def test_handmade_lists_skip_invalid_entries():
+@pytest.mark.parametrize("precision", ["bf16", "mix", "fp8"])
+def test_handmade_lists_skip_invalid_entries(precision):
     """rf_sparse_attn accepts any list: -1 and out-of-range ids are skipped, counts clamped."""
     import torch
     import block_sparse_video_rf_amd as rf
-    w, _ = SMALL["minimax_small"]
+    w = SMALL["minimax_small"][0].with_(precision=precision)
     desc = rf.Desc.from_workload(w)
     q, k, v = make_qkv(w)
     res = run_gpu(desc, q, k, v)
@@ -203,16 +205,15 @@ def test_handmade_lists_skip_invalid_entries():
             valid_num[qb, n] = len(good)
     num = np.minimum(num, nB)
     out_p = torch.empty_like(b.out_p)
-    rf.rf_sparse_attn(desc, b.qp, b.kp, b.vpt, None, None, None, None, None,
+    rf.rf_sparse_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, b.v_scale,
                       torch.from_numpy(idx).cuda(), torch.from_numpy(num).cuda(), nB, out_p)
     torch.cuda.synchronize()
     g = geometry_of(desc)
-    p = plan(g)
-    pi = permutation(g)
-    ref = oracle.sparse_attention(oracle.permute_rows(f32(q), pi), oracle.permute_rows(f32(k), pi),
-                                  oracle.permute_rows(f32(v), pi), p, valid_idx, valid_num,
-                                  1.0 / np.sqrt(w.head_dim))
-    assert_close(f32(to_host_u16(out_p)), ref, BF16_TOL, "handmade lists")
+    # The oracle on the valid entries only, with the precision's own quantisation.
+    ref = oracle.run(f32(q), f32(k), f32(v), g, precision=precision,
+                     select=(valid_idx, valid_num))["out_p"]
+    assert_close(f32(to_host_u16(out_p)), ref, FP8_TOL if precision == "fp8" else BF16_TOL,
+                 f"handmade lists ({precision})")
 
 
 def test_recomputed_pools_and_determinism():

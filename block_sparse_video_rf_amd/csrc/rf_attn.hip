@@ -3,7 +3,7 @@
 //
 // One workgroup of 8 waves per (batch, query block, query head). Wave w owns
 // query rows [32 rg, 32 rg + 32) of the block (rg = w % 4) and one half of the
-// keys of every listed block (kh = w / 4). The workgroup walks its list of key
+// keys of every listed block (kh = 1 - w / 4). The workgroup walks its list of key
 // blocks, staging K (row-major, [128][D]) and V (already block-transposed by
 // the permute kernel, [D][128]) in LDS, and each wave computes
 //
@@ -362,7 +362,7 @@ __device__ __forceinline__ void mfma_steps(MfmaCtx<D, PREC>& c) {
 
 // Workgroup of 8 waves per (batch, query block, head). Wave w owns query rows
 // [32 rg, 32 rg + 32) with rg = w % 4 and key rows [64 kh, 64 kh + 64) of every
-// listed block with kh = w / 4: each wave keeps its own running max / sum /
+// listed block with kh = 1 - w / 4: each wave keeps its own running max / sum /
 // O^T over its half of the keys, and the two halves are merged through LDS at
 // the end (exact: the merge rescales both to the common maximum).
 //
@@ -415,7 +415,11 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   // branches on kh are scalar branches.
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64, li = lane % 32, h = lane / 32;
-  const int rg = wave & 3, kh = wave >> 2;
+  // Waves 4..7 are dispatched later and lose issue and LDS arbitration to
+  // waves 0..3 on their SIMD (measured: their MFMA intervals run longer,
+  // whatever their role, and s_setprio does not change it). The key half
+  // that runs one interval behind goes to the favoured waves 0..3.
+  const int rg = wave & 3, kh = (wave >> 2) ^ 1;
   const int gt = tid & 255;  // thread index within its kh group
   int32_t b, q, n;
   decode_wg(g, blockIdx.x, &b, &q, &n);

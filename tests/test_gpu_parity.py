@@ -261,3 +261,31 @@ def test_selection_paths_by_sparse_count(grid):
     swaps = check_selection(p, 1, 1, b.select_idx.cpu().numpy(), b.select_num.cpu().numpy(),
                             scores)
     log(f"  selection exact ({swaps} near-tie rows)")
+
+
+@pytest.mark.parametrize("precision", ["bf16", "mix", "fp8"])
+def test_reference_raised_mid_row(precision):
+    """Keys in the second half of the sequence scaled by 100: their logits exceed
+    the reference the first blocks set by far more than 2^64 allows, so the
+    softmax raises it (and rescales) in the middle of every row."""
+    import block_sparse_video_rf_amd as rf
+    from synth import bf16_from_f32
+    w = _custom("grow", 1, 2, 2, 64, 128, (9, 16, 32), True, 0.0, precision=precision)
+    desc = rf.Desc.from_workload(w)
+    q, k, v = make_qkv(w)
+    kf = f32(k)
+    half = w.seq_len // 2
+    kf[:, :, half:, :] *= 100.0
+    k = bf16_from_f32(kf)
+    res = run_gpu(desc, q, k, v)
+    assert res["bufs"].info.dense_fallback == 1   # every block listed, in order
+    g = geometry_of(desc)
+    ref = oracle.run(f32(q), f32(k), f32(v), g, precision=precision)["out"]
+    # Logits this large make every row peaked, so little averaging hides the bf16
+    # rounding of P (2^-9 relative) and of the output: together at most
+    # 2^-9 * (max|v - O| + |O|), about 2.4e-2 for |v| <= 4. In fp8 a P that
+    # rounds to the neighbouring E4M3 code (fp32 against float64 logits at a
+    # rounding midpoint) moves a two-key row by w (1 - w) / 8 * |v1 - v2|, at
+    # most 0.25. A wrong rescale would show in the mean, which keeps its bound.
+    tol = (0.25, FP8_TOL[1]) if precision == "fp8" else (4e-2, BF16_TOL[1])
+    assert_close(f32(to_host_u16(res["out"])), ref, tol, f"raised mid-row ({precision})")

@@ -72,6 +72,11 @@ __device__ __forceinline__ void store_stream(void* p, uint32_t x, uint32_t y, ui
 __device__ __forceinline__ void store_stream(void* p, uint32_t x, uint32_t y) {
   __builtin_nontemporal_store(v2u{x, y}, reinterpret_cast<v2u*>(p));
 }
+// Streaming 16-byte load of an input read exactly once.
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  const v4u x = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
 
 // Smallest e with amax <= 448 * 2^e, clamped to [-126, 127] (a normal fp32
 // power of two); 0 for amax == 0. With amax = f * 2^x, f in [0.5, 1), and
@@ -139,8 +144,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
     const int i = p * RPP + rsub;
     if (i < len) {
       const int64_t nat = rf_natural_row(g, row0 + i);
-      val[p] = *reinterpret_cast<const uint4*>(src + rf_row_offset(g, g.layout, heads, b, n, nat) +
-                                               c * 8);
+      val[p] = load_stream(src + rf_row_offset(g, g.layout, heads, b, n, nat) + c * 8);
     } else {
       val[p] = make_uint4(0, 0, 0, 0);
     }
@@ -315,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(UnpermuteArgs a) {
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int i = p * RPP + rsub;
-    if (i < len) val[p] = *reinterpret_cast<const uint4*>(src + (int64_t)i * D + c * 8);
+    if (i < len) val[p] = load_stream(src + (int64_t)i * D + c * 8);
   }
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {

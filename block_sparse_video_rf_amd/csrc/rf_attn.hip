@@ -15,7 +15,9 @@
 // Computing the transposed products makes every lane own one query row
 // (column l % 32 of the 32x32 accumulator tiles), so the row maximum, the
 // running sum and the rescale of O are lane-local except for one exchange
-// with the partner lane l ^ 32 for the maximum.
+// with the partner lane l ^ 32 for the maximum (when one is needed: bf16 and
+// mix take the exponentials against the running reference and compute a
+// maximum only when a block's sums say the reference must rise).
 //
 // K rows are fed to the A operand in a permuted order (kappa(), which swaps
 // bits 2 and 3 of the tile row) so that the 16 accumulator values of a lane
@@ -31,6 +33,12 @@
 // The mix precision replaces the QK^T operands by fp8 E4M3 codes
 // (v_mfma_scale_f32_32x32x64_f8f6f4, unit block scales) and folds
 // scale * q_scale * k_scale of the block pair into the exponent multiplier.
+// The fp8 precision also runs O^T on E4M3 codes: V^T codes with the block's
+// power-of-two scale as the product's E8M0 operand scale, and P quantised to
+// E4M3 against an integer reference (the ceiling of the running maximum, so
+// the largest P lies in (128, 256]); an extra product of an all-ones operand
+// with P^T gives the row sums of the rounded P. With no lists (the dense
+// path) every block is visited in order.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>

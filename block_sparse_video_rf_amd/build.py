@@ -67,5 +67,17 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_abi_check() -> str:
+    """Compile the tests' native C-ABI check program against the built library
+    (host code only; it finds librf.so next to the package through its rpath)."""
+    src = os.path.join(os.path.dirname(PKG), "tests", "native", "abi_check.cpp")
+    exe = os.path.join(os.path.dirname(src), "abi_check")
+    if not os.path.exists(src):
+        return ""
+    _run([HIPCC, "-O2", "-std=c++17", "-I", INCLUDE, src, "-L", PKG, "-lrf",
+          "-Wl,-rpath," + PKG, "-Wl,-rpath,$ORIGIN/../../block_sparse_video_rf_amd", "-o", exe])
+    return exe
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

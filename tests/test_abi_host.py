@@ -100,7 +100,21 @@ BAD = [
     ("geometry_ff", dict(first_frame_rows=100), 8),
     ("geometry_grid", dict(grid=(9, 0, 32)), 8),
     ("precision_bad", dict(precision=9), 11),
+    # 8193 sparse blocks (one 8-row strip of 8193 tiles): one more than the
+    # selection kernel holds
+    ("sparse_limit", dict(grid=(3, 8, 8 * 8193), first_frame_rows=8 * 8 * 8193,
+                          seq_len=128 + 3 * 8 * 8 * 8193), 10),
 ]
+
+
+def test_sparse_block_limit_accepted():
+    """Exactly 8192 sparse blocks is the largest accepted geometry."""
+    d = _good()
+    d.grid = (3, 8, 8 * 8192)
+    d.first_frame_rows = 8 * 8 * 8192
+    d.seq_len = 128 + 3 * 8 * 8 * 8192
+    info = rf.rf_plan(d)
+    assert info.n_sparse == 8192 and info.dense_fallback == 0
 
 
 @pytest.mark.parametrize("name,change,status", BAD, ids=[b[0] for b in BAD])

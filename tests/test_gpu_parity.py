@@ -235,10 +235,12 @@ def test_recomputed_pools_and_determinism():
     assert torch.equal(idx2, b.select_idx) and torch.equal(num2, b.select_num)
 
 
-@pytest.mark.parametrize("grid", [(5, 16, 1200), (3, 16, 8400)], ids=["nS600", "nS2100"])
+@pytest.mark.parametrize("grid", [(5, 16, 1200), (3, 16, 8400), (3, 8, 65536)],
+                         ids=["nS600", "nS2100", "nS8192"])
 def test_selection_paths_by_sparse_count(grid):
-    """Selection alone at 600 sparse blocks (16 keys per lane) and at 2100 (above
-    the register path: one workgroup per row), against the oracle's rule."""
+    """Selection alone at 600 sparse blocks (16 keys per lane), at 2100 (above
+    the register path: one workgroup per row) and at 8192 (the largest accepted,
+    the workgroup path's LDS full), against the oracle's rule."""
     import torch
     import block_sparse_video_rf_amd as rf
     w = _custom("sel", 1, 1, 1, 64, 128, grid, True, 0.8)

@@ -67,6 +67,16 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_mfma_peak() -> str:
+    """Compile the matrix-core microbenchmark that bench.py --peaks runs."""
+    src = os.path.join(os.path.dirname(PKG), "tests", "native", "mfma_peak.cpp")
+    exe = os.path.join(os.path.dirname(src), "mfma_peak")
+    if not os.path.exists(src):
+        return ""
+    _run([HIPCC, *HIP_FLAGS, src, "-o", exe])
+    return exe
+
+
 def build_abi_check() -> str:
     """Compile the tests' native C-ABI check program against the built library
     (host code only; it finds librf.so next to the package through its rpath)."""

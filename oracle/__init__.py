@@ -23,6 +23,9 @@ Sources (cited by page title and section throughout):
   constraint list.
 * "RainFusion2.0: Temporal-Spatial Awareness and Hardware-Efficient
   Block-wise Sparse Attention" - the paper abstract.
+* "MXAttention: Data-Free Optimal Scaling and Pre-Normalization Quantization
+  for MXFP4 Attention" - the abstract (the 7.25 scaling boundary; quantising
+  the exponentials before the row sum).
 
 Parity pins: every function here is pinned by a CPU test in
 ``tests/test_oracle_*.py`` against page facts, closed forms, brute force or an
@@ -31,9 +34,11 @@ quality (it needs trained models and a video benchmark): parity unpinned.
 """
 from .geometry import Geometry, plan, permutation, permute_rows, unpermute_rows, block_rows
 from .select import pool_blocks, block_scores, topk_sparse, select_lists, num_kept
-from .attention import sparse_attention, attention_block, attention_block_fp8p
+from .attention import sparse_attention, attention_block, attention_block_fp8p, attention_block_mxp
 from .fp8 import (e4m3_decode, e4m3_encode, e4m3_round, quantize_blocks, quantize_blocks_pow2,
                   pow2_scale_exponent)
+from .mxfp4 import (e2m1_decode, e2m1_encode, e2m1_round, mx_scale_exponent, quantize_rows_mx,
+                    quantize_v_mx, dequantize_rows_mx, dequantize_v_mx, mx_round_groups)
 from .pipeline import run
 
 __all__ = [
@@ -41,5 +46,7 @@ __all__ = [
     "pool_blocks", "block_scores", "topk_sparse", "select_lists", "num_kept",
     "sparse_attention", "attention_block", "attention_block_fp8p", "e4m3_decode",
     "e4m3_encode", "e4m3_round", "quantize_blocks", "quantize_blocks_pow2",
-    "pow2_scale_exponent", "run",
+    "pow2_scale_exponent", "run", "attention_block_mxp", "e2m1_decode", "e2m1_encode",
+    "e2m1_round", "mx_scale_exponent", "quantize_rows_mx", "quantize_v_mx", "dequantize_rows_mx",
+    "dequantize_v_mx", "mx_round_groups",
 ]

@@ -35,6 +35,22 @@ Scaling by 2**k commutes with E4M3 rounding of normal values, so a one-pass
 kernel that holds a smaller integer reference for earlier blocks rounds them
 the same way; only values below 2**-6 (subnormal, below 2**-14 of the largest
 P) can round differently, and their weight is negligible.
+
+"mxfp4" precision ("RainFusion Attention", Wan2.2 T2V quantization, names it;
+MXAttention, abstract, gives the pre-normalisation step). Reading, in the same
+shape as "fp8":
+
+* ``t_c`` and ``M = ceil(max_c t_c)`` as above, ``x_c = 2**(t_c - M)`` in (0, 1];
+* the row's keys fall into MX blocks of 32: the quarters of each listed
+  128-row block (``mxfp4.py``); each block of ``x`` is quantised to MXFP4
+  with its own UOS scale, giving ``P_c``;
+* ``O = sum_c P_c v_c / sum_c P_c``.
+
+Each MX block carries its own power-of-two scale, so multiplying ``x`` by
+``2**k`` multiplies every ``P_c`` by exactly ``2**k``: any integer reference
+gives the same output, and a one-pass kernel that rescales by powers of two
+matches this definition (up to the clamp of the scale at 2**-127, far below
+the largest P).
 """
 from __future__ import annotations
 
@@ -42,6 +58,7 @@ import numpy as np
 
 from .fp8 import e4m3_round
 from .geometry import Plan
+from .mxfp4 import MX_BLOCK, mx_round_groups
 
 
 def attention_block(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
@@ -68,6 +85,34 @@ def attention_block_fp8p(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: flo
     return (pq @ np.asarray(v, dtype=np.float64)) / pq.sum(axis=1, keepdims=True)
 
 
+def attention_block_mxp(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                        groups) -> np.ndarray:
+    """Attention with MXFP4 probabilities quantised before the row sum (float64).
+
+    ``q [M, D]`` against ``k, v [L, D]`` (already dequantised operands);
+    ``groups``: the MX blocks of P as ``(start, stop)`` key ranges covering
+    [0, L)."""
+    q = np.asarray(q, dtype=np.float64)
+    if k.shape[0] == 0:
+        return np.zeros((q.shape[0], v.shape[1]), dtype=np.float64)
+    t = (scale / np.log(2.0)) * (q @ np.asarray(k, dtype=np.float64).T)
+    ref = np.ceil(t.max(axis=1, keepdims=True))
+    pq = mx_round_groups(np.exp2(t - ref), groups)
+    return (pq @ np.asarray(v, dtype=np.float64)) / pq.sum(axis=1, keepdims=True)
+
+
+def listed_groups(p: Plan, ids):
+    """MX blocks of the listed keys: the quarters of each listed block's real
+    rows, as ranges into the concatenation that ``listed_rows`` returns."""
+    groups, off = [], 0
+    for j in ids:
+        n = p.blocks[j][1]
+        for a in range(0, n, MX_BLOCK):
+            groups.append((off + a, off + min(a + MX_BLOCK, n)))
+        off += n
+    return groups
+
+
 def listed_rows(p: Plan, ids) -> np.ndarray:
     """Permuted row indices covered by the listed block ids, in list order."""
     parts = [np.arange(p.blocks[j][0], p.blocks[j][0] + p.blocks[j][1]) for j in ids]
@@ -75,15 +120,20 @@ def listed_rows(p: Plan, ids) -> np.ndarray:
 
 
 def sparse_attention(qp, kp, vp, p: Plan, select_idx, select_num, scale: float,
-                     query_blocks=None, quantize_p: bool = False) -> np.ndarray:
+                     query_blocks=None, quantize_p=False) -> np.ndarray:
     """Permuted-order attention output ``[B, N1, S, D]`` (float64).
 
     ``qp``: ``[B, N1, S, D]``; ``kp``, ``vp``: ``[B, N2, S, D]`` (permuted rows,
     any real dtype). ``query_blocks``: optional iterable of ``(b, q, n)`` to
     evaluate only those (query block, head) pairs; other rows stay zero.
-    ``quantize_p``: E4M3 probabilities ("fp8" precision, ``attention_block_fp8p``).
+    ``quantize_p``: False; True or "fp8" for E4M3 probabilities
+    (``attention_block_fp8p``); "mxfp4" for MXFP4 probabilities
+    (``attention_block_mxp``).
     """
-    block = attention_block_fp8p if quantize_p else attention_block
+    if quantize_p not in (False, True, "fp8", "mxfp4"):
+        raise ValueError(f"quantize_p must be False, True, 'fp8' or 'mxfp4', got {quantize_p!r}")
+    mx = quantize_p == "mxfp4"
+    block = attention_block_fp8p if quantize_p in (True, "fp8") else attention_block
     B, N1, S, D = qp.shape
     G = N1 // kp.shape[1]
     nB = p.n_blocks
@@ -95,6 +145,7 @@ def sparse_attention(qp, kp, vp, p: Plan, select_idx, select_num, scale: float,
         row = b * nB + q
         ids = select_idx[row, n, :select_num[row, n]]
         rows = listed_rows(p, ids)
-        out[b, n, r0:r0 + m] = block(qp[b, n, r0:r0 + m], kp[b, n // G, rows],
-                                     vp[b, n // G, rows], scale)
+        args = (qp[b, n, r0:r0 + m], kp[b, n // G, rows], vp[b, n // G, rows], scale)
+        out[b, n, r0:r0 + m] = (attention_block_mxp(*args, listed_groups(p, ids)) if mx
+                                else block(*args))
     return out

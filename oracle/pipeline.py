@@ -8,8 +8,9 @@ TEST INFRASTRUCTURE (see the package docstring).
 4. exact softmax attention over the listed blocks (``attention.py``),
    with Q/K replaced by their fp8 E4M3 dequantised values in "mix" and "fp8"
    precision, V by its power-of-two-scaled E4M3 values and P by E4M3
-   exponentials in "fp8" (``fp8.py``, ``attention.py``); selection always uses
-   the unquantised Q/K;
+   exponentials in "fp8" (``fp8.py``, ``attention.py``); in "mxfp4" every
+   operand and P in MXFP4 with UOS scales (``mxfp4.py``, ``attention.py``);
+   selection always uses the unquantised Q/K;
 5. undo the arrangement.
 """
 from __future__ import annotations
@@ -20,6 +21,7 @@ import numpy as np
 
 from .attention import sparse_attention
 from .fp8 import e4m3_decode, quantize_blocks, quantize_blocks_pow2
+from .mxfp4 import dequantize_rows_mx, dequantize_v_mx, quantize_rows_mx, quantize_v_mx
 from .geometry import Geometry, permutation, permute_rows, plan, unpermute_rows
 from .select import block_scores, pool_blocks, select_lists
 
@@ -79,10 +81,19 @@ def run(q, k, v, g: Geometry, scale: float | None = None, precision: str = "bf16
             v8, sv = quantize_blocks_pow2(vp, p)
             res.update(v8=v8, v_scale=sv)
             v_att = e4m3_decode(v8) * _expand_block_scale(sv, p, S)
+    elif precision == "mxfp4":
+        q4, eq = quantize_rows_mx(qp)
+        k4, ek = quantize_rows_mx(kp)
+        v4, ev = quantize_v_mx(vp, p)
+        res.update(q4=q4, k4=k4, v4=v4, q_exp=eq, k_exp=ek, v_exp=ev)
+        q_att = dequantize_rows_mx(q4, eq)
+        k_att = dequantize_rows_mx(k4, ek)
+        v_att = dequantize_v_mx(v4, ev, p)
     elif precision != "bf16":
-        raise ValueError(f"precision must be bf16, mix or fp8, got {precision!r}")
+        raise ValueError(f"precision must be bf16, mix, fp8 or mxfp4, got {precision!r}")
+    qmode = {"fp8": "fp8", "mxfp4": "mxfp4"}.get(precision, False)
     out_p = sparse_attention(q_att, k_att, v_att, p, sel[0], sel[1], scale, query_blocks,
-                             quantize_p=precision == "fp8")
+                             quantize_p=qmode)
     res["out_p"] = out_p
     out = unpermute_rows(out_p, pi)
     if layout == "TND":

@@ -37,13 +37,30 @@
 // power-of-two scale as the product's E8M0 operand scale, and P quantised to
 // E4M3 against an integer reference (the ceiling of the running maximum, so
 // the largest P lies in (128, 256]); an extra product of an all-ones operand
-// with P^T gives the row sums of the rounded P. With no lists (the dense
-// path) every block is visited in order.
+// with P^T gives the row sums of the rounded P. The mxfp4 precision runs both
+// products on E2M1 codes with one E8M0 scale per 32 values of each operand
+// lane (the MX block of the hardware: a lane's 32 contraction values): Q and
+// K scales per 32 channels, V^T scales per 32 keys, and P quantised per lane
+// (its 32 keys of one query row) with the scale rule of rf_mx.h, against the
+// same integer reference as fp8. With no lists (the dense path) every block is
+// visited in order.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
 
 #include "rf_internal.h"
+#include "rf_mx.h"
+
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+// The scaled 32x32x64 product with E2M1 operands in 4 registers each: the
+// v4i32 overload of the LLVM intrinsic (the clang builtin only takes the
+// 8-register operands of fp8). cbsz = blgp = 4 selects E2M1; opsel picks the
+// byte of each lane's 32-bit scale word that holds its E8M0 scale.
+__device__ f32x16_t rf_mfma_scale_fp4(i32x4 a, i32x4 b, f32x16_t c, int cbsz, int blgp,
+                                      int opsel_a, int scale_a, int opsel_b, int scale_b)
+    __asm("llvm.amdgcn.mfma.scale.f32.32x32x64.f8f6f4.v4i32.v4i32");
 
 namespace {
 
@@ -63,9 +80,9 @@ struct AttnArgs {
   const uint16_t* vpt;
   const uint8_t* q8;
   const uint8_t* k8;
-  const float* q_scale;
-  const float* k_scale;
-  const float* v_scale;
+  const void* q_scale;  // fp32 per block (mix, fp8); E8M0 bytes (mxfp4)
+  const void* k_scale;
+  const void* v_scale;
   const int32_t* select_idx;
   const int32_t* select_num;
   int32_t max_kv;
@@ -136,9 +153,11 @@ typedef const float __attribute__((address_space(4)))* scale_ptr;
 // maxima (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-// Raw buffer descriptor over [base, base + bytes): a load past the end
-// returns zeros. (Third dword: the raw 32-bit data format used for plain
-// byte-addressed buffers on gfx9.)
+// Raw buffer descriptor over [base, base + bytes): a load whose VGPR offset
+// is past the end returns zeros. Only the VGPR offset (with the instruction's
+// immediate) is range-checked, not the SGPR offset, so every load below puts
+// its whole offset in the VGPR operand. (Third dword: the raw 32-bit data
+// format used for plain byte-addressed buffers on gfx9.)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
@@ -180,11 +199,12 @@ __device__ __forceinline__ float max_halves(float x) {
 }
 
 // Operand modes: bf16 products; mix (fp8 E4M3 S^T = K Q^T, bf16 O^T); fp8
-// (both products on E4M3 codes).
+// (both products on E4M3 codes); mxfp4 (both products on E2M1 codes).
 template <int PREC>
 struct Prec {
-  static constexpr bool QK8 = PREC != RF_PREC_BF16;  // S^T on E4M3 codes
-  static constexpr bool V8 = PREC == RF_PREC_FP8;    // O^T on E4M3 codes
+  static constexpr bool QK8 = PREC != RF_PREC_BF16;  // S^T on quantised codes
+  static constexpr bool F4 = PREC == RF_PREC_MXFP4;  // E2M1 operands, per-lane E8M0 scales
+  static constexpr bool VQ = PREC == RF_PREC_FP8 || F4;  // O^T on codes, P quantised
 };
 
 // Operand schedule of one MFMA interval: the S^T products of this block
@@ -193,20 +213,20 @@ struct Prec {
 // an fp8 product takes two.
 template <int D, int PREC>
 struct MfmaPlan {
-  static constexpr bool QK8 = Prec<PREC>::QK8, V8 = Prec<PREC>::V8;
+  static constexpr bool QK8 = Prec<PREC>::QK8, VQ = Prec<PREC>::VQ, F4 = Prec<PREC>::F4;
   static constexpr int DT = D / 32;
   static constexpr int QK_STEPS = QK8 ? D / 64 : D / 16;
-  static constexpr int S_RPM = QK8 ? 2 : 1;          // reads per S^T product
+  static constexpr int S_RPM = QK8 && !F4 ? 2 : 1;   // reads per S^T product
   static constexpr int NS_MFMA = 2 * QK_STEPS;       // S^T products (2 key tiles)
   static constexpr int NS_READ = NS_MFMA * S_RPM;
   // O^T products: DT channel tiles x the wave's 64 keys in k-steps of 16
-  // (bf16) or one k-step of 64 (fp8).
-  static constexpr int NPV = V8 ? DT : 4 * DT;
-  static constexpr int PV_RPM = V8 ? 2 : 1;          // reads per O^T product
+  // (bf16) or one k-step of 64 (fp8, mxfp4).
+  static constexpr int NPV = VQ ? DT : 4 * DT;
+  static constexpr int PV_RPM = VQ && !F4 ? 2 : 1;   // reads per O^T product
   static constexpr int NREAD = NS_READ + NPV * PV_RPM;
-  // fp8: one more product, of an all-ones A operand with P^T, accumulates the
-  // row sums of the rounded P (no LDS reads).
-  static constexpr int NSUM = V8 ? 1 : 0;
+  // fp8, mxfp4: one more product, of an all-ones A operand with P^T,
+  // accumulates the row sums of the rounded P (no LDS reads).
+  static constexpr int NSUM = VQ ? 1 : 0;
   static constexpr int NMFMA = NS_MFMA + NPV + NSUM;
   static constexpr int NR = 8;                       // fragments in flight
   static constexpr int NPRE = NR < NS_READ ? NR : NS_READ;  // K reads issued before the barrier
@@ -242,11 +262,17 @@ struct MfmaCtx {
   f32x16 s[2];
   f32x16 o[P::DT];
   bf16x8 qf[P::QK8 ? 1 : P::QK_STEPS];
-  i32x8 qf8[P::QK8 ? P::QK_STEPS : 1];
+  i32x8 qf8[P::QK8 && !P::F4 ? P::QK_STEPS : 1];
+  i32x4 qf4[P::F4 ? P::QK_STEPS : 1];  // Q fragment (E2M1 codes), mxfp4
   bf16x8 pf16[2][2];              // P^T operands, bf16 O^T products
   i32x8 pf8;                      // P^T operand (E4M3 codes), fp8 O^T products
+  i32x4 pf4;                      // P^T operand (E2M1 codes), mxfp4 O^T products
   int vexp;                       // E8M0 scale of the previous block's V (fp8)
-  f32x16 osum;                    // fp8: every value is the running row sum of P
+  // mxfp4 E8M0 scale words (byte = scale of one operand lane's 32 values):
+  // Q (byte 2 st: k-step st), K per key tile (likewise), V^T of the previous
+  // block (byte e: channel tile e), P^T (byte 0).
+  int qsc, ksc[2], vsc, psc;
+  f32x16 osum;                    // fp8, mxfp4: every value is the running row sum of P
 };
 
 // Bytes per row of a K tile and of a V^T tile in global memory, and their
@@ -254,10 +280,16 @@ struct MfmaCtx {
 // banks).
 template <int D, int PREC>
 struct TileGeom {
-  static constexpr int KROW = Prec<PREC>::QK8 ? D : 2 * D;
-  static constexpr int VROW = Prec<PREC>::V8 ? 128 : 256;
+  static constexpr bool F4 = Prec<PREC>::F4;
+  static constexpr int KROW = F4 ? D / 2 : (Prec<PREC>::QK8 ? D : 2 * D);
+  static constexpr int VROW = F4 ? 64 : (Prec<PREC>::VQ ? 128 : 256);
   static constexpr int KSTR = KROW + 16;
   static constexpr int VSTR = VROW + 16;
+  // mxfp4: the E8M0 bytes that follow a tile in LDS: D/32 per K row (in the
+  // rows' LDS order), 4 x D per V^T tile (the layout rf_permute writes); both
+  // 4 D bytes.
+  static constexpr int KSC = F4 ? 128 * (D / 32) : 0;
+  static constexpr int VSC = F4 ? 4 * D : 0;
 };
 
 // LDS byte offset of read R relative to its base (compile-time).
@@ -268,10 +300,11 @@ __device__ __forceinline__ const uint8_t* read_addr(const MfmaCtx<D, PREC>& c) {
   if constexpr (R < P::NS_READ) {
     // S^T product sm: key tile t (LDS rows 32 t + [0, 32)), channel k-step st.
     constexpr int sm = R / P::S_RPM, half = R % P::S_RPM, st = sm / 2, t = sm % 2;
-    return c.kbase + 32 * t * TG::KSTR + (P::QK8 ? 64 * st + 16 * half : 32 * st);
-  } else if constexpr (P::V8) {
-    // O^T product e (channel tile): 32 key bytes of V^T row 32 e + li.
-    constexpr int pr = R - P::NS_READ, e = pr / 2, half = pr % 2;
+    return c.kbase + 32 * t * TG::KSTR + (P::QK8 && !P::F4 ? 64 * st + 16 * half : 32 * st);
+  } else if constexpr (P::VQ) {
+    // O^T product e (channel tile): the lane's 32 keys of V^T row 32 e + li
+    // (32 bytes of E4M3, 16 of E2M1).
+    constexpr int pr = R - P::NS_READ, e = pr / P::PV_RPM, half = pr % P::PV_RPM;
     return c.vbase + 32 * e * TG::VSTR + 16 * half;
   } else {
     constexpr int pm = R - P::NS_READ, tu = pm / P::DT, e = pm % P::DT;
@@ -308,7 +341,7 @@ __device__ __forceinline__ void pin_products(MfmaCtx<D, PREC>& c) {
   pin_acc(c.s[1]);
 #pragma unroll
   for (int e = 0; e < MfmaPlan<D, PREC>::DT; ++e) pin_acc(c.o[e]);
-  if constexpr (Prec<PREC>::V8) pin_acc(c.osum);
+  if constexpr (Prec<PREC>::VQ) pin_acc(c.osum);
 }
 
 template <int NR, int R>
@@ -323,7 +356,11 @@ __device__ __forceinline__ void mfma_steps(MfmaCtx<D, PREC>& c) {
   if constexpr (M < MEND) {
     if constexpr (M < P::NS_MFMA) {
       constexpr int st = M / 2, t = M % 2;
-      if constexpr (P::QK8) {
+      if constexpr (P::F4) {
+        const uint4 x = ring_slot<M % P::NR>(c.ring);
+        const i32x4 ka = {(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+        c.s[t] = rf_mfma_scale_fp4(ka, c.qf4[st], c.s[t], 4, 4, 2 * st, c.ksc[t], 2 * st, c.qsc);
+      } else if constexpr (P::QK8) {
         const i32x8 ka = ring_pair<P::NR, 2 * M>(c.ring);
         c.s[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, c.qf8[st], c.s[t], 0, 0, 0,
                                                                  127, 0, 127);
@@ -332,14 +369,28 @@ __device__ __forceinline__ void mfma_steps(MfmaCtx<D, PREC>& c) {
         __builtin_memcpy(&ka, &ring_slot<M % P::NR>(c.ring), 16);
         c.s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, c.qf[st], c.s[t], 0, 0, 0);
       }
-    } else if constexpr (P::V8 && M == P::NS_MFMA + P::NPV) {
+    } else if constexpr (P::VQ && M == P::NS_MFMA + P::NPV) {
       // Row sums: (all-ones 32 x 64) x P^T puts the sum of this lane's query row
-      // over the wave's 64 keys in every accumulator value (E4M3 1.0 = 0x38).
-      constexpr int k1 = 0x38383838;
-      const i32x8 ones = {k1, k1, k1, k1, k1, k1, k1, k1};
-      c.osum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, c.pf8, c.osum, 0, 0, 0, 127,
-                                                               0, 127);
-    } else if constexpr (P::V8) {
+      // over the wave's 64 keys in every accumulator value (E4M3 1.0 = 0x38,
+      // E2M1 1.0 = 0x2).
+      if constexpr (P::F4) {
+        constexpr int k1 = 0x22222222;
+        const i32x4 ones = {k1, k1, k1, k1};
+        c.osum = rf_mfma_scale_fp4(ones, c.pf4, c.osum, 4, 4, 0, 127, 0, c.psc);
+      } else {
+        constexpr int k1 = 0x38383838;
+        const i32x8 ones = {k1, k1, k1, k1, k1, k1, k1, k1};
+        c.osum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, c.pf8, c.osum, 0, 0, 0,
+                                                                 127, 0, 127);
+      }
+    } else if constexpr (P::F4) {
+      // O^T tile e += V^T (E2M1, scale byte e of vsc) P^T (E2M1, scale psc)
+      // over the wave's 64 keys.
+      constexpr int e = M - P::NS_MFMA;
+      const uint4 x = ring_slot<(P::NS_READ + e) % P::NR>(c.ring);
+      const i32x4 va = {(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+      c.o[e] = rf_mfma_scale_fp4(va, c.pf4, c.o[e], 4, 4, e, c.vsc, 0, c.psc);
+    } else if constexpr (P::VQ) {
       // O^T tile e += 2^(vexp - 127) V^T (E4M3) P^T (E4M3) over the wave's 64 keys.
       constexpr int e = M - P::NS_MFMA;
       const i32x8 va = ring_pair<P::NR, P::NS_READ + 2 * e>(c.ring);
@@ -365,6 +416,18 @@ __device__ __forceinline__ void mfma_steps(MfmaCtx<D, PREC>& c) {
     // its use and leave too few in flight.
     __builtin_amdgcn_sched_barrier(0);
     mfma_steps<D, PREC, M + 1, MEND>(c);
+  }
+}
+
+// mxfp4 O^T products of the last block (after the loop): one per channel tile,
+// the tile index being the opsel immediate of the V^T scale.
+template <int D, int PREC, int E = 0>
+__device__ __forceinline__ void pv_tail_fp4(MfmaCtx<D, PREC>& c, const uint8_t* vs) {
+  if constexpr (E < D / 32) {
+    const uint4 x = *reinterpret_cast<const uint4*>(vs + 32 * E * TileGeom<D, PREC>::VSTR);
+    const i32x4 va = {(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+    c.o[E] = rf_mfma_scale_fp4(va, c.pf4, c.o[E], 4, 4, E, c.vsc, 0, c.psc);
+    pv_tail_fp4<D, PREC, E + 1>(c, vs);
   }
 }
 
@@ -397,8 +460,9 @@ template <int D, int PREC, bool ALL>
 __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   using PL = MfmaPlan<D, PREC>;
   using TG = TileGeom<D, PREC>;
-  constexpr bool MIX = PL::QK8;           // E4M3 Q/K (mix and fp8)
-  constexpr bool V8 = PL::V8;             // E4M3 V and P (fp8)
+  constexpr bool MIX = PL::QK8;           // quantised Q/K (mix, fp8, mxfp4)
+  constexpr bool VQ = PL::VQ;             // quantised V and P (fp8, mxfp4)
+  constexpr bool F4 = PL::F4;             // E2M1 codes with E8M0 scales (mxfp4)
   constexpr int KROW = TG::KROW;          // K row bytes in global memory
   constexpr int KSTR = TG::KSTR;          // K row stride in LDS (bytes, padded)
   constexpr int VROW = TG::VROW;          // V^T row bytes (128 keys)
@@ -409,11 +473,14 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   constexpr int K_CH = 128 * KCH / 256;   // K chunks per thread of the kh = 1 group
   constexpr int V_CH = D * VCH / 256;     // V^T chunks per thread of the kh = 0 group
   constexpr int NSTG = K_CH > V_CH ? K_CH : V_CH;
-  constexpr int KT = 128 * KSTR, VT = D * VSTR;
+  constexpr int KSC = TG::KSC, VSC = TG::VSC;  // mxfp4 scale bytes after each tile
+  constexpr int NSC = KSC / 16;           // their 16-byte chunks (K and V alike)
+  static_assert(KSC == VSC, "scale chunks");
+  constexpr int KT = 128 * KSTR + KSC, VT = D * VSTR + VSC;
   constexpr int TILE_BYTES = 2 * KT + 2 * VT;
   constexpr int MERGE_BYTES = 4 * (DT * 16 + 2) * 64 * 4;
-  static_assert(MERGE_BYTES <= TILE_BYTES, "merge buffer");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[TILE_BYTES];
+  __shared__ __attribute__((aligned(16)))
+  uint8_t smem[TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES];
   uint8_t* const kbuf0 = smem;
   uint8_t* const vbuf0 = smem + 2 * KT;
 
@@ -441,7 +508,26 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   MfmaCtx<D, PREC> c;
   // Q fragment (B operand of S^T = K Q^T): query row qrow, channels by k-step.
   float q_sigma = 1.0f;
-  if constexpr (MIX) {
+  if constexpr (F4) {
+    // E2M1 codes: channels [64 st + 32 h, +32) are bytes [32 st + 16 h, +16);
+    // the row's D/32 scale bytes shifted so that byte 2 st holds block 2 st + h.
+    const int64_t qrow_g = ((int64_t)b * g.N1 + n) * g.S + row0 + qrow;
+    const uint8_t* qr = a.q8 + qrow_g * (D / 2);
+#pragma unroll
+    for (int st = 0; st < PL::QK_STEPS; ++st) {
+      if (qvalid) {
+        const uint4 x = *reinterpret_cast<const uint4*>(qr + 32 * st + 16 * h);
+        c.qf4[st] = i32x4{(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+      } else {
+        c.qf4[st] = i32x4{0, 0, 0, 0};
+      }
+    }
+    const uint8_t* qs = static_cast<const uint8_t*>(a.q_scale) + qrow_g * DT;
+    const uint32_t w = !qvalid ? 0u
+                       : (DT == 4 ? *reinterpret_cast<const uint32_t*>(qs)
+                                  : (uint32_t)*reinterpret_cast<const uint16_t*>(qs));
+    c.qsc = (int)(w >> (8 * h));
+  } else if constexpr (MIX) {
     const uint8_t* qr = a.q8 + (((int64_t)b * g.N1 + n) * g.S + row0 + qrow) * D;
 #pragma unroll
     for (int st = 0; st < PL::QK_STEPS; ++st) {
@@ -454,7 +540,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
         c.qf8[st] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
       }
     }
-    q_sigma = a.q_scale[((int64_t)b * g.N1 + n) * g.n_blocks + q];
+    q_sigma = static_cast<const float*>(a.q_scale)[((int64_t)b * g.N1 + n) * g.n_blocks + q];
   } else {
     const uint16_t* qr = a.qp + (((int64_t)b * g.N1 + n) * g.S + row0 + qrow) * D;
 #pragma unroll
@@ -477,6 +563,9 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) c.pf16[t][u] = bf16x8{};
   c.pf8 = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  c.pf4 = i32x4{0, 0, 0, 0};
+  c.psc = 0;
+  c.vsc = 0;
   c.osum = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
 
@@ -486,14 +575,16 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   cnt = cnt < 0 ? 0 : (cnt > a.max_kv ? a.max_kv : cnt);
 
   const uint8_t* kbytes =
-      MIX ? a.k8 + ((int64_t)b * g.N2 + nk) * g.S * D
+      MIX ? a.k8 + ((int64_t)b * g.N2 + nk) * g.S * KROW
           : reinterpret_cast<const uint8_t*>(a.kp + ((int64_t)b * g.N2 + nk) * g.S * D);
   const uint8_t* vbytes = reinterpret_cast<const uint8_t*>(a.vpt) +
                           ((int64_t)b * g.N2 + nk) * g.n_blocks * (int64_t)D * VROW;
   const scale_ptr kscale =
-      MIX ? (scale_ptr)(a.k_scale + ((int64_t)b * g.N2 + nk) * g.n_blocks) : nullptr;
+      MIX && !F4 ? (scale_ptr)(static_cast<const float*>(a.k_scale) + ((int64_t)b * g.N2 + nk) * g.n_blocks)
+                 : nullptr;
   const scale_ptr vscale =
-      V8 ? (scale_ptr)(a.v_scale + ((int64_t)b * g.N2 + nk) * g.n_blocks) : nullptr;
+      VQ && !F4 ? (scale_ptr)(static_cast<const float*>(a.v_scale) + ((int64_t)b * g.N2 + nk) * g.n_blocks)
+                : nullptr;
 
   // Tile copies: buffer loads over this (batch, kv head)'s K and V^T.
   const __amdgpu_buffer_rsrc_t rk = raw_buffer(kbytes, (uint32_t)(g.S * KROW));
@@ -504,24 +595,61 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     rf_block_rows(g, jb, &r0, &fl);
     return (int)(r0 * KROW);
   };
-  // K rows past a short block's end are whatever follows in memory (zeros past
-  // the end of K); they are masked out of the softmax.
+  // mxfp4 scale bytes of this (batch, kv head): K [S][D/32], V [n_blocks][4][D].
+  const __amdgpu_buffer_rsrc_t rks =
+      F4 ? raw_buffer(static_cast<const uint8_t*>(a.k_scale) + ((int64_t)b * g.N2 + nk) * g.S * DT,
+                      (uint32_t)(g.S * DT))
+         : raw_buffer(nullptr, 0);
+  const __amdgpu_buffer_rsrc_t rvs =
+      F4 ? raw_buffer(static_cast<const uint8_t*>(a.v_scale) +
+                          ((int64_t)b * g.N2 + nk) * g.n_blocks * (int64_t)VSC,
+                      (uint32_t)((int64_t)g.n_blocks * VSC))
+         : raw_buffer(nullptr, 0);
+  // K rows past a short block's end are the next rows of K, or zeros past the
+  // end of this (batch, kv head)'s K (and K scales): the offsets are range
+  // checked. They are masked out of the softmax.
   // (Named registers rather than an array: they must never live in scratch.)
   static_assert(NSTG <= 8, "staging size");
   u32x4 st0, st1, st2, st3, st4, st5, st6, st7;
+  u32x4 sts;  // mxfp4: one 16-byte chunk of the staged tile's scale bytes
+  static_assert(NSC <= 256, "scale chunks per group");
 #define RF_GLD1(VAR, M)                                                                    \
   if constexpr ((M) < NSTG) {                                                              \
-    if ((M) < nch_) VAR = __builtin_amdgcn_raw_buffer_load_b128(rs_, gt * 16, so_ + (M) * 4096, 0); \
+    if ((M) < nch_) VAR = __builtin_amdgcn_raw_buffer_load_b128(rs_, gt * 16 + so_ + (M) * 4096, 0, 0); \
   }
 #define RF_KST1(BUF, VAR, M)                                                               \
   if constexpr ((M) < K_CH) {                                                              \
     const int slot_ = (M) * 256 + gt, r_ = slot_ / KCH, c_ = slot_ % KCH;                  \
-    *reinterpret_cast<u32x4*>((BUF) + (V8 ? kslot8(r_) : r_) * KSTR + c_ * 16) = VAR;      \
+    *reinterpret_cast<u32x4*>((BUF) + (VQ ? kslot8(r_) : r_) * KSTR + c_ * 16) = VAR;      \
   }
 #define RF_VST1(BUF, VAR, M)                                                               \
   if constexpr ((M) < V_CH) {                                                              \
     const int slot_ = (M) * 256 + gt, d_ = slot_ / VCH, c_ = slot_ % VCH;                  \
     *reinterpret_cast<u32x4*>((BUF) + d_ * VSTR + c_ * 16) = VAR;                          \
+  }
+// mxfp4 scale chunk: V^T scales copied as they are; K scales of rows
+// 16/DT * gt .. (DT bytes each) placed by row like the K rows, in runs of 4
+// rows (kslot8 keeps the low two bits of the row).
+#define RF_GLDS(RS, SO)                                                                    \
+  if constexpr (F4) {                                                                      \
+    if (gt < NSC) sts = __builtin_amdgcn_raw_buffer_load_b128((RS), gt * 16 + (SO), 0, 0); \
+  }
+#define RF_VSST(BUF)                                                                       \
+  if constexpr (F4) {                                                                      \
+    if (gt < NSC) *reinterpret_cast<u32x4*>((BUF) + D * VSTR + gt * 16) = sts;             \
+  }
+#define RF_KSST(BUF)                                                                       \
+  if constexpr (F4) {                                                                      \
+    if (gt < NSC) {                                                                        \
+      uint8_t* ks_ = (BUF) + 128 * KSTR;                                                   \
+      const int r_ = gt * (16 / DT);                                                       \
+      if constexpr (DT == 4) {                                                             \
+        *reinterpret_cast<u32x4*>(ks_ + kslot8(r_) * 4) = sts;                             \
+      } else {                                                                             \
+        *reinterpret_cast<uint2*>(ks_ + kslot8(r_) * 2) = uint2{sts.x, sts.y};             \
+        *reinterpret_cast<uint2*>(ks_ + kslot8(r_ + 4) * 2) = uint2{sts.z, sts.w};         \
+      }                                                                                    \
+    }                                                                                      \
   }
 // Tile J into the staging registers: K rows (as 16-byte chunks, row-major)
 // or V^T. Chunk m of thread gt is bytes [16 (256 m + gt), +16) of the tile in
@@ -533,7 +661,11 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     RF_GLD1(st0, 0) RF_GLD1(st1, 1) RF_GLD1(st2, 2) RF_GLD1(st3, 3)                        \
     RF_GLD1(st4, 4) RF_GLD1(st5, 5) RF_GLD1(st6, 6) RF_GLD1(st7, 7)                        \
   } while (0)
-#define RF_LOAD_K(J) RF_LOAD_TILE(rk, k_tile_off(J), K_CH)
+#define RF_LOAD_K(J)                                                                       \
+  do {                                                                                     \
+    RF_LOAD_TILE(rk, k_tile_off(J), K_CH);                                                 \
+    RF_GLDS(rks, k_tile_off(J) / KROW * DT)                                                \
+  } while (0)
 #define RF_STORE_K(BUF)                                                                    \
   do {                                                                                     \
     RF_KST1(BUF, st0, 0) RF_KST1(BUF, st1, 1) RF_KST1(BUF, st2, 2) RF_KST1(BUF, st3, 3)    \
@@ -563,9 +695,11 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     if (kh == 0) {
       RF_LOAD_K(safe(w0));
       RF_STORE_K(kbuf0);
+      RF_KSST(kbuf0)
     } else {
       RF_LOAD_K(safe(w1));
       RF_STORE_K(kbuf0 + KT);
+      RF_KSST(kbuf0 + KT)
     }
     for (int x = tid; x < VT / 16; x += kThreads8)
       reinterpret_cast<uint4*>(vbuf0 + VT)[x] = uint4{0, 0, 0, 0};
@@ -576,13 +710,36 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   // This lane's fragment bases: K row 64 kh + kappa(li) (+ 32 t) (fp8: LDS row
   // 64 kh + li (+ 32 t), holding key 64 kh + 16 t + kappa8(li)), V^T row li
   // (+ 32 e) at key column 64 kh + 8 h (+ 16 k-step) (fp8: 64 kh + 32 h).
-  const int krow = V8 ? li : kappa(li);
-  const int koff = (64 * kh + krow) * KSTR + (MIX ? 32 * h : 16 * h);
-  const int voff = V8 ? li * VSTR + 64 * kh + 32 * h : li * VSTR + 2 * (64 * kh + 8 * h);
+  // mxfp4: bytes of E2M1, half of fp8's.
+  const int krow = VQ ? li : kappa(li);
+  const int koff = (64 * kh + krow) * KSTR + (MIX && !F4 ? 32 * h : 16 * h);
+  const int voff = F4   ? li * VSTR + 32 * kh + 16 * h
+                   : VQ ? li * VSTR + 64 * kh + 32 * h
+                        : li * VSTR + 2 * (64 * kh + 8 * h);
+  // mxfp4 scale words of a K tile for this lane's rows (LDS rows 64 kh + 32 t
+  // + li, as its K fragments), shifted so that byte 2 st is channel block
+  // 2 st + h.
+  auto read_ksc = [&](const uint8_t* kbuf) {
+    if constexpr (F4) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint8_t* p = kbuf + 128 * KSTR + (64 * kh + 32 * t + li) * DT;
+        const uint32_t w = DT == 4 ? *reinterpret_cast<const uint32_t*>(p)
+                                   : (uint32_t)*reinterpret_cast<const uint16_t*>(p);
+        c.ksc[t] = (int)(w >> (8 * h));
+      }
+    }
+  };
+  // LDS operations the barrier after the K prefetch leaves in flight: the
+  // fragment reads, and (mxfp4) one more for the two scale reads, which the
+  // compiler may issue as one instruction or two (either way every earlier
+  // store has completed at that count).
+  constexpr int NKEEP = PL::NPRE + (F4 ? 1 : 0);
   c.vexp = 127;
   int par = 0;  // parity of block i: its K tile sits in K buffer par
   c.kbase = kbuf0 + koff;
   issue_reads<D, PREC, 0, PL::NPRE>(c);
+  read_ksc(kbuf0);
   for (int i = 0; i < cnt; ++i) {
     const int32_t j = safe(w0);
     int64_t kr0;
@@ -595,6 +752,12 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
 
     // ---- MFMA interval ----
     c.vbase = vbuf0 + (par ^ 1) * VT + voff;  // V^T of the previous block
+    if constexpr (F4) {
+      // Its scale bytes: quarter 2 kh + h, channels 32 e + li for e < DT.
+      const uint8_t* p = vbuf0 + (par ^ 1) * VT + D * VSTR + (2 * kh + h) * D + DT * li;
+      c.vsc = DT == 4 ? (int)*reinterpret_cast<const uint32_t*>(p)
+                      : (int)*reinterpret_cast<const uint16_t*>(p);
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t) c.s[t] = f32x16{};
     issue_reads<D, PREC, PL::NPRE, PL::NR>(c);
@@ -609,6 +772,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
       RF_GLD1(st0, 0)
       mfma_steps<D, PREC, RF_Q(1), RF_Q(2)>(c);
       RF_GLD1(st1, 1)
+      RF_GLDS(kh == 0 ? rvs : rks, kh == 0 ? jcopy * VSC : so_ / KROW * DT)
       mfma_steps<D, PREC, RF_Q(2), RF_Q(3)>(c);
       RF_GLD1(st2, 2)
       mfma_steps<D, PREC, RF_Q(3), RF_Q(4)>(c);
@@ -633,10 +797,12 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     if (kh == 0) {
       // V^T of block i into buffer par (read in the next two intervals).
       RF_STORE_V(vbuf0 + par * VT);
+      RF_VSST(vbuf0 + par * VT)
     } else {
       // K of block i + 2 into buffer par (block i's K was last read in the
       // MFMA interval just done).
       RF_STORE_K(kbuf0 + par * KT);
+      RF_KSST(kbuf0 + par * KT)
     }
 
     // Mask rows past a short block's end (all rows of a masked block).
@@ -645,25 +811,30 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int kv = V8 ? 64 * kh + 32 * h + 16 * t + v
+          const int kv = VQ ? 64 * kh + 32 * h + 16 * t + v
                             : 64 * kh + 32 * t + 16 * (v / 8) + 8 * h + (v % 8);
           if (kv >= klen) c.s[t][v] = -INFINITY;
         }
     }
 
+    // mix and fp8 fold the block scales of Q and K into the exponent
+    // multiplier; mxfp4 applies its scales inside the products (kscale is not
+    // set there).
     float cs = a.scale_log2;
-    if constexpr (MIX) cs *= q_sigma * kscale[j];
+    if constexpr (MIX && !F4) cs *= q_sigma * kscale[j];
 
-    // Row maximum over this wave's keys (then the partner half-wave), times cs.
-    auto block_max = [&]() -> float {
+    // Maximum of this lane's raw scores; the row maximum over this wave's keys
+    // (then the partner half-wave), times cs.
+    auto lane_max = [&]() -> float {
       float m0 = c.s[0][0], m1 = c.s[1][0];
 #pragma unroll
       for (int v = 1; v < 15; v += 2) {
         m0 = max3f(m0, c.s[0][v], c.s[0][v + 1]);
         m1 = max3f(m1, c.s[1][v], c.s[1][v + 1]);
       }
-      return max_halves(max3f(m0, m1, max3f(c.s[0][15], c.s[1][15], c.s[1][15]))) * cs;
+      return max3f(m0, m1, max3f(c.s[0][15], c.s[1][15], c.s[1][15]));
     };
+    auto block_max = [&]() -> float { return max_halves(lane_max()) * cs; };
     // O^T holds every product up to the previous block here, exactly what a
     // rescale of the running state must cover.
     auto rescale = [&](float m_new, float alpha) {
@@ -673,27 +844,47 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
       for (int e = 0; e < DT; ++e)
 #pragma unroll
         for (int v = 0; v < 16; ++v) c.o[e][v] *= alpha;
-      if constexpr (V8) {
+      if constexpr (VQ) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) c.osum[v] *= alpha;
       }
     };
     // While every key so far is masked m_run is -inf; any finite stand-in keeps
     // exp2(-inf - m) at 0 instead of NaN.
-    auto ref_neg = [&]() -> float { return (V8 ? 8.0f : 0.0f) - fmaxf(m_run, -1e30f); };
+    auto ref_neg = [&]() -> float { return (VQ && !F4 ? 8.0f : 0.0f) - fmaxf(m_run, -1e30f); };
 
     float lsum = 0.0f;
-    if constexpr (V8) {
+    if constexpr (VQ) {
       // fp8: P = 2^(t - m_run + 8) goes to E4M3 (largest finite 448), so m_run
       // is the integer ceiling of the running maximum, raised as soon as a
       // block exceeds it: the largest P stays in (128, 256], and the rescale by
       // a power of two is exact and leaves the rounding of normal P unchanged.
-      const float mc = block_max();
+      // mxfp4: P = 2^(t - m_run) in MX blocks of the lane's 32 keys, with the
+      // same integer reference (the block scale absorbs any power of two).
+      const float lm = lane_max();
+      const float mc = max_halves(lm) * cs;
       if (__any(mc > m_run)) {
         const float m_new = fmaxf(m_run, ceilf(mc));
         rescale(m_new, m_run == -INFINITY ? 0.0f : ldexpf(1.0f, (int)(m_run - m_new)));
       }
       const float mneg = ref_neg();
+      if constexpr (F4) {
+        // The lane's MX block: its largest P fixes the exponent e (rf_mx.h);
+        // the codes are E2M1 of P / 2^e, taken as 2^(t - m_run - e) (e is an
+        // integer, exact in the exponent). Nibble 16 t + v of the B operand
+        // is key 32 h + 16 t + v. Row sums: the all-ones product.
+        const int ep = rf_mx_scale_exp(__builtin_amdgcn_exp2f(fmaf(lm, cs, mneg)));
+        const float mneg_e = mneg - (float)ep;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int t = w / 2, v0 = 8 * (w % 2);
+          float p[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) p[x] = __builtin_amdgcn_exp2f(fmaf(c.s[t][v0 + x], cs, mneg_e));
+          c.pf4[w] = (int)rf_e2m1_pack8(p);
+        }
+        c.psc = ep + 127;
+      } else {
       // P as E4M3 codes (round to nearest even; P <= 2^8 < 448), byte 16 t + v
       // of the B operand. The row sum of the rounded values (what multiplies
       // V) comes from the all-ones product in the next MFMA interval.
@@ -708,6 +899,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
         c.pf8[w] = pk;
       }
       c.vexp = (int)((__float_as_uint(vscale[j]) >> 23) & 0xffu);
+      }
     } else {
       // bf16 P and fp32 sums hold exponentials far beyond 1, so the reference
       // m_run is only a guard against overflow: the exponentials are taken
@@ -745,7 +937,8 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     c.kbase = kbuf0 + par * KT + koff;
     __builtin_amdgcn_sched_barrier(0);
     issue_reads<D, PREC, 0, PL::NPRE>(c);
-    lds_barrier_keep<PL::NPRE>();
+    read_ksc(kbuf0 + par * KT);
+    lds_barrier_keep<NKEEP>();
     w0 = w1;
     w1 = w2;
     w2 = w3;
@@ -754,7 +947,15 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   // O^T += V^T P^T of the last block.
   if (cnt > 0) {
     const uint8_t* vs = vbuf0 + (par ^ 1) * VT + voff;
-    if constexpr (V8) {
+    if constexpr (F4) {
+      const uint8_t* p = vbuf0 + (par ^ 1) * VT + D * VSTR + (2 * kh + h) * D + DT * li;
+      c.vsc = DT == 4 ? (int)*reinterpret_cast<const uint32_t*>(p)
+                      : (int)*reinterpret_cast<const uint16_t*>(p);
+      pv_tail_fp4<D, PREC>(c, vs);
+      constexpr int k1 = 0x22222222;
+      const i32x4 ones = {k1, k1, k1, k1};
+      c.osum = rf_mfma_scale_fp4(ones, c.pf4, c.osum, 4, 4, 0, 127, 0, c.psc);
+    } else if constexpr (VQ) {
 #pragma unroll
       for (int e = 0; e < DT; ++e) {
         const uint4 x0 = *reinterpret_cast<const uint4*>(vs + 32 * e * VSTR);
@@ -782,7 +983,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     }
   }
   if (kh == 0) lds_barrier();  // matches the kh = 1 group's extra barrier
-  if constexpr (V8) l_run = c.osum[0];  // the row sum over this wave's keys (any value)
+  if constexpr (VQ) l_run = c.osum[0];  // the row sum over this wave's keys (any value)
 
 #undef RF_LOAD_K
 #undef RF_STORE_K
@@ -791,6 +992,9 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
 #undef RF_LOAD_TILE
 #undef RF_KST1
 #undef RF_VST1
+#undef RF_GLDS
+#undef RF_VSST
+#undef RF_KSST
 
   __syncthreads();  // every wave is done with the tiles
   // Merge the two key halves: wave (rg, 1) hands its state to wave (rg, 0).
@@ -814,7 +1018,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   // bf16 and mix: each lane summed the keys of its own half-wave, so the row
   // sum adds the partner lane's. fp8: the all-ones product already gave every
   // lane the sum over all the wave's keys.
-  if constexpr (!V8) lt += __shfl_xor(lt, 32);
+  if constexpr (!VQ) lt += __shfl_xor(lt, 32);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (qvalid) {
     uint16_t* orow = a.out_p + (((int64_t)b * g.N1 + n) * g.S + row0 + qrow) * D;
@@ -840,11 +1044,12 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
 
 rf_status rf_launch_sparse_attn(const RfGeom& g, int32_t precision, float scale, const void* qp,
                                 const void* kp, const void* vpt, const uint8_t* q8,
-                                const uint8_t* k8, const float* q_scale, const float* k_scale,
-                                const float* v_scale, const int32_t* select_idx,
+                                const uint8_t* k8, const void* q_scale, const void* k_scale,
+                                const void* v_scale, const int32_t* select_idx,
                                 const int32_t* select_num, int32_t max_kv, void* out_p,
                                 void* stream) {
-  if (precision != RF_PREC_BF16 && precision != RF_PREC_MIX && precision != RF_PREC_FP8)
+  if (precision != RF_PREC_BF16 && precision != RF_PREC_MIX && precision != RF_PREC_FP8 &&
+      precision != RF_PREC_MXFP4)
     return RF_ERR_PRECISION;
   AttnArgs a;
   a.g = g;
@@ -865,21 +1070,26 @@ rf_status rf_launch_sparse_attn(const RfGeom& g, int32_t precision, float scale,
   if (wgs > 0x7fffffff) return RF_ERR_SHAPE;
   // Tile loads address one (batch, kv head)'s K and V^T through 32-bit buffer
   // offsets.
-  const int64_t krow = precision == RF_PREC_BF16 ? 2 * g.D : g.D;
-  const int64_t vrow = precision == RF_PREC_FP8 ? 128 : 256;
+  const int64_t krow =
+      precision == RF_PREC_BF16 ? 2 * g.D : (precision == RF_PREC_MXFP4 ? g.D / 2 : g.D);
+  const int64_t vrow =
+      precision == RF_PREC_FP8 ? 128 : (precision == RF_PREC_MXFP4 ? 64 : 256);
   if (g.S * krow > 0x7fffffff || (int64_t)g.n_blocks * g.D * vrow > 0x7fffffff) return RF_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((uint32_t)wgs);
   const bool all = select_idx == nullptr;
   // One instantiation per (head_dim, precision, lists or none).
   using Kern = void (*)(AttnArgs);
-  static const Kern kernels[2][3][2] = {
+  static const Kern kernels[2][4][2] = {
       {{sparse_attn_kernel<64, RF_PREC_BF16, false>, sparse_attn_kernel<64, RF_PREC_BF16, true>},
        {sparse_attn_kernel<64, RF_PREC_MIX, false>, sparse_attn_kernel<64, RF_PREC_MIX, true>},
-       {sparse_attn_kernel<64, RF_PREC_FP8, false>, sparse_attn_kernel<64, RF_PREC_FP8, true>}},
+       {sparse_attn_kernel<64, RF_PREC_FP8, false>, sparse_attn_kernel<64, RF_PREC_FP8, true>},
+       {sparse_attn_kernel<64, RF_PREC_MXFP4, false>, sparse_attn_kernel<64, RF_PREC_MXFP4, true>}},
       {{sparse_attn_kernel<128, RF_PREC_BF16, false>, sparse_attn_kernel<128, RF_PREC_BF16, true>},
        {sparse_attn_kernel<128, RF_PREC_MIX, false>, sparse_attn_kernel<128, RF_PREC_MIX, true>},
-       {sparse_attn_kernel<128, RF_PREC_FP8, false>, sparse_attn_kernel<128, RF_PREC_FP8, true>}}};
+       {sparse_attn_kernel<128, RF_PREC_FP8, false>, sparse_attn_kernel<128, RF_PREC_FP8, true>},
+       {sparse_attn_kernel<128, RF_PREC_MXFP4, false>,
+        sparse_attn_kernel<128, RF_PREC_MXFP4, true>}}};
   hipLaunchKernelGGL(kernels[g.D == 128][precision][all], grid, dim3(kThreads8), 0, s, a);
   return hipGetLastError() == hipSuccess ? RF_OK : RF_ERR_HIP;
 }

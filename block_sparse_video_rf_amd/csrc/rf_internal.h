@@ -96,16 +96,16 @@ rf_status rf_derive(const rf_desc* d, RfGeom* g, rf_plan_info* info);
 // Launchers (one per .hip file).
 rf_status rf_launch_permute(const RfGeom& g, int32_t precision, const void* q, const void* k,
                             const void* v, void* qp, void* kp, void* vpt, float* q_pool,
-                            float* k_pool, uint8_t* q8, uint8_t* k8, float* q_scale,
-                            float* k_scale, float* v_scale, void* stream);
+                            float* k_pool, uint8_t* q8, uint8_t* k8, void* q_scale,
+                            void* k_scale, void* v_scale, void* stream);
 rf_status rf_launch_unpermute(const RfGeom& g, const void* out_p, void* out, void* stream);
 rf_status rf_launch_pool_select(const RfGeom& g, float scale, const void* qp, const void* kp,
                                 const float* q_pool, const float* k_pool, int32_t* select_idx,
                                 int32_t* select_num, int32_t max_kv, void* ws, void* stream);
 rf_status rf_launch_sparse_attn(const RfGeom& g, int32_t precision, float scale, const void* qp,
                                 const void* kp, const void* vpt, const uint8_t* q8,
-                                const uint8_t* k8, const float* q_scale, const float* k_scale,
-                                const float* v_scale, const int32_t* select_idx,
+                                const uint8_t* k8, const void* q_scale, const void* k_scale,
+                                const void* v_scale, const int32_t* select_idx,
                                 const int32_t* select_num, int32_t max_kv, void* out_p,
                                 void* stream);
 

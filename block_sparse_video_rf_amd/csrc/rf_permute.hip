@@ -1,5 +1,5 @@
-// Arrangement kernels: permute (+ block-mean pooling, + fp8 E4M3 quantisation
-// for the mix precision) and the inverse permutation.
+// Arrangement kernels: permute (+ block-mean pooling, + quantisation of the
+// fp8-family and mxfp4 precisions) and the inverse permutation.
 //
 // "RainFusion Attention" (introduction, Geometry handling) and the xLLM
 // pull request "feat: add RainFusion sparse attention for wan2.2" (commit
@@ -18,9 +18,16 @@
 // kernel's PV product reads its MFMA operand with contiguous 16-byte LDS
 // loads; the transpose goes through LDS here, where the work is bandwidth
 // bound anyway.
+//
+// mxfp4 (OCP MXFP4 with the MXAttention scale rule, abstract: power-of-two
+// scales with the boundary 7.25): Q and K rows in blocks of 32 channels, V in
+// the 32-key quarters of each block per channel; each block's exponent e is
+// the smallest with amax <= 7.25 * 2^e, stored as the E8M0 byte e + 127, and
+// its values as E2M1 codes of x / 2^e (nearest even, saturating at 6).
 #include <hip/hip_runtime.h>
 
 #include "rf_internal.h"
+#include "rf_mx.h"
 
 namespace {
 
@@ -38,9 +45,10 @@ struct PermuteArgs {
   float* k_pool;
   uint8_t* q8;
   uint8_t* k8;
-  float* q_scale;
-  float* k_scale;
-  float* v_scale;  // fp8 precision: V as E4M3 codes (vpt) with power-of-two scales
+  void* q_scale;  // fp32 per block (mix, fp8) or E8M0 bytes per 32 channels (mxfp4)
+  void* k_scale;
+  void* v_scale;  // fp8: fp32 power-of-two V scales; mxfp4: E8M0 bytes per key quarter
+  int mx;         // mxfp4 precision
 };
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -155,6 +163,48 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
   if (kind == 2) {
     // V: stage the block in LDS, then write it transposed [D][128] with zero
     // columns past the block's length.
+    if (a.mx) {
+      // mxfp4: thread (channel d, part) quantises QPT consecutive key quarters
+      // of channel d; codes of V^T two keys per byte ([D][64] bytes), the
+      // quarter's E8M0 byte at row g, position DT (d % 32) + d / 32.
+      constexpr int DT = D / 32;
+      constexpr int QPT = 4 * D / kThreads;  // quarters per thread: 2 (D=128) or 1
+      constexpr int TPD = 4 / QPT;           // threads per channel
+      uint16_t* tile = reinterpret_cast<uint16_t*>(red);  // [128][D + 8]
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        const int i = p * RPP + rsub;
+        *reinterpret_cast<uint4*>(tile + i * (D + 8) + c * 8) = val[p];
+      }
+      __syncthreads();
+      const int64_t blk = ((int64_t)b * g.N2 + n) * g.n_blocks + j;
+      uint8_t* dst = reinterpret_cast<uint8_t*>(a.vpt) + blk * (int64_t)D * 64;
+      uint8_t* sdst = reinterpret_cast<uint8_t*>(a.v_scale) + blk * 4 * D;
+      const int d = tid / TPD, part = tid % TPD;
+      uint32_t w[4 * QPT];
+#pragma unroll
+      for (int qq = 0; qq < QPT; ++qq) {
+        const int gq = part * QPT + qq;
+        float x[32];
+        float amax = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+          x[r] = __uint_as_float((uint32_t)tile[(32 * gq + r) * (D + 8) + d] << 16);
+          amax = fmaxf(amax, fabsf(x[r]));
+        }
+        const int ex = rf_mx_scale_exp(amax);
+#pragma unroll
+        for (int r = 0; r < 32; ++r) x[r] = ldexpf(x[r], -ex);
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) w[4 * qq + k4] = rf_e2m1_pack8(x + 8 * k4);
+        sdst[gq * D + DT * (d % 32) + d / 32] = (uint8_t)(ex + 127);
+      }
+#pragma unroll
+      for (int qq = 0; qq < QPT; ++qq)
+        store_stream(dst + d * 64 + (part * QPT + qq) * 16, w[4 * qq], w[4 * qq + 1],
+                     w[4 * qq + 2], w[4 * qq + 3]);
+      return;
+    }
     if (a.v_scale) {
       // fp8: E4M3 codes of x / 2^e with the block's power-of-two scale 2^e
       // (exact scaling), same transposed layout in bytes.
@@ -195,7 +245,8 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
         }
         store_stream(dst + d * 128 + cc * 16, w[0], w[1], w[2], w[3]);
       }
-      if (tid == 0) a.v_scale[((int64_t)b * g.N2 + n) * g.n_blocks + j] = ldexpf(1.0f, ex);
+      if (tid == 0)
+        static_cast<float*>(a.v_scale)[((int64_t)b * g.N2 + n) * g.n_blocks + j] = ldexpf(1.0f, ex);
       return;
     }
     uint16_t* tile = reinterpret_cast<uint16_t*>(red);  // [128][D + 8]
@@ -259,8 +310,39 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
     __syncthreads();
   }
 
-  // Mix precision: per-block E4M3 codes and scale.
   uint8_t* q8 = kind == 0 ? a.q8 : a.k8;
+  // mxfp4: E2M1 codes of each row's 32-channel blocks (4 adjacent threads hold
+  // one block: 8 channels each) and one E8M0 byte per block.
+  if (a.mx && q8) {
+    constexpr int DT = D / 32;
+    uint8_t* sc = reinterpret_cast<uint8_t*>(kind == 0 ? a.q_scale : a.k_scale);
+    const int64_t rbase = ((int64_t)b * heads + n) * g.S + row0;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int i = p * RPP + rsub;
+      const uint32_t w[4] = {val[p].x, val[p].y, val[p].z, val[p].w};
+      float x[8];
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bf_lo(w[e]);
+        x[2 * e + 1] = bf_hi(w[e]);
+        amax = fmaxf(amax, fmaxf(fabsf(x[2 * e]), fabsf(x[2 * e + 1])));
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      amax = fmaxf(amax, __shfl_xor(amax, 2));
+      const int ex = rf_mx_scale_exp(amax);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = ldexpf(x[e], -ex);
+      const uint32_t codes = rf_e2m1_pack8(x);
+      if (i < len) {
+        *reinterpret_cast<uint32_t*>(q8 + (rbase + i) * (D / 2) + c * 4) = codes;
+        if (c % 4 == 0) sc[(rbase + i) * DT + c / 4] = (uint8_t)(ex + 127);
+      }
+    }
+    return;
+  }
+  // Mix precision: per-block E4M3 codes and scale.
   if (q8) {
     float amax = 0.0f;
 #pragma unroll
@@ -290,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
         store_stream(q8 + base + (int64_t)i * D + c * 8, lo, hi);
       }
     }
-    float* sc = kind == 0 ? a.q_scale : a.k_scale;
+    float* sc = static_cast<float*>(kind == 0 ? a.q_scale : a.k_scale);
     if (tid == 0) sc[((int64_t)b * heads + n) * g.n_blocks + j] = sigma;
   }
 }
@@ -336,10 +418,10 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(UnpermuteArgs a) {
 
 rf_status rf_launch_permute(const RfGeom& g, int32_t precision, const void* q, const void* k,
                             const void* v, void* qp, void* kp, void* vpt, float* q_pool,
-                            float* k_pool, uint8_t* q8, uint8_t* k8, float* q_scale,
-                            float* k_scale, float* v_scale, void* stream) {
-  (void)precision;
+                            float* k_pool, uint8_t* q8, uint8_t* k8, void* q_scale,
+                            void* k_scale, void* v_scale, void* stream) {
   PermuteArgs a;
+  a.mx = precision == RF_PREC_MXFP4;
   a.g = g;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);

@@ -18,8 +18,8 @@ LIB_PATH = os.path.join(PKG, "librf.so")
 
 LAYOUT_BNSD, LAYOUT_TND = 0, 1
 DTYPE_BF16, DTYPE_FP16 = 0, 1
-PREC_BF16, PREC_MIX, PREC_FP8 = 0, 1, 2
-_PREC = {"bf16": PREC_BF16, "mix": PREC_MIX, "fp8": PREC_FP8}
+PREC_BF16, PREC_MIX, PREC_FP8, PREC_MXFP4 = 0, 1, 2, 3
+_PREC = {"bf16": PREC_BF16, "mix": PREC_MIX, "fp8": PREC_FP8, "mxfp4": PREC_MXFP4}
 _LAYOUT = {"BNSD": LAYOUT_BNSD, "TND": LAYOUT_TND}
 
 
@@ -46,6 +46,9 @@ class RfPlanInfo(ctypes.Structure):
         ("q_pool_elems", ctypes.c_int64), ("k_pool_elems", ctypes.c_int64),
         ("q_scale_elems", ctypes.c_int64), ("k_scale_elems", ctypes.c_int64),
         ("v_scale_elems", ctypes.c_int64), ("ws_select_bytes", ctypes.c_size_t),
+        ("q8_bytes", ctypes.c_int64), ("k8_bytes", ctypes.c_int64), ("vpt_bytes", ctypes.c_int64),
+        ("q_scale_bytes", ctypes.c_int64), ("k_scale_bytes", ctypes.c_int64),
+        ("v_scale_bytes", ctypes.c_int64),
     ]
 
     def as_dict(self):
@@ -217,7 +220,9 @@ class Buffers:
     selectIdx / selectNum, the selection workspace): the dense path needs none.
     In mix and fp8 precision Q/K exist only as E4M3 codes (``q8``, ``k8``) with
     per-block scales; in fp8 ``vpt`` holds one-byte E4M3 codes and ``v_scale``
-    their power-of-two block scales.
+    their power-of-two block scales. In mxfp4 precision ``q8``, ``k8`` and
+    ``vpt`` hold E2M1 codes two per byte and the scales are E8M0 bytes (one per
+    32 channels of a Q/K row, one per channel and 32-key quarter of a V block).
     """
 
     def __init__(self, desc: Desc, device="cuda", lists: bool = True):
@@ -227,19 +232,35 @@ class Buffers:
         B, N1, N2, S, D = desc.batch, desc.heads_q, desc.heads_kv, desc.seq_len, desc.head_dim
         nB, nS = info.n_blocks, info.n_sparse
         bf = torch.bfloat16
-        mix = desc.precision in ("mix", "fp8", PREC_MIX, PREC_FP8)   # E4M3 Q/K
-        v8 = desc.precision in ("fp8", PREC_FP8)                       # E4M3 V
+        prec = _PREC[desc.precision] if isinstance(desc.precision, str) else int(desc.precision)
+        mix = prec != PREC_BF16               # quantised Q/K
+        v8 = prec in (PREC_FP8, PREC_MXFP4)   # quantised V
+        f4 = prec == PREC_MXFP4
+        u8, f32 = torch.uint8, torch.float32
         self.qp = None if mix else torch.empty((B, N1, S, D), dtype=bf, device=device)
         self.kp = None if mix else torch.empty((B, N2, S, D), dtype=bf, device=device)
-        self.vpt = torch.empty((B, N2, nB, D, 128), dtype=torch.uint8 if v8 else bf, device=device)
-        self.v_scale = torch.empty((B, N2, nB), dtype=torch.float32, device=device) if v8 else None
-        f32 = torch.float32
+        if f4:
+            self.vpt = torch.empty((B, N2, nB, D, 64), dtype=u8, device=device)
+            self.v_scale = torch.empty((B, N2, nB, 4, D), dtype=u8, device=device)
+            self.q8 = torch.empty((B, N1, S, D // 2), dtype=u8, device=device)
+            self.k8 = torch.empty((B, N2, S, D // 2), dtype=u8, device=device)
+            self.q_scale = torch.empty((B, N1, S, D // 32), dtype=u8, device=device)
+            self.k_scale = torch.empty((B, N2, S, D // 32), dtype=u8, device=device)
+        else:
+            self.vpt = torch.empty((B, N2, nB, D, 128), dtype=u8 if v8 else bf, device=device)
+            self.v_scale = torch.empty((B, N2, nB), dtype=f32, device=device) if v8 else None
+            self.q8 = torch.empty((B, N1, S, D), dtype=u8, device=device) if mix else None
+            self.k8 = torch.empty((B, N2, S, D), dtype=u8, device=device) if mix else None
+            self.q_scale = torch.empty((B, N1, nB), dtype=f32, device=device) if mix else None
+            self.k_scale = torch.empty((B, N2, nB), dtype=f32, device=device) if mix else None
+        # Every precision-dependent buffer has the size rf_plan gives for it.
+        for name in ("q8", "k8", "vpt", "q_scale", "k_scale", "v_scale"):
+            t = getattr(self, name)
+            nbytes = 0 if t is None else t.numel() * t.element_size()
+            if nbytes != getattr(info, name + "_bytes"):
+                raise AssertionError(f"{name}: {nbytes} bytes, rf_plan says {getattr(info, name + '_bytes')}")
         self.q_pool = torch.empty((B, N1, nS, D), dtype=f32, device=device) if lists else None
         self.k_pool = torch.empty((B, N2, nS, D), dtype=f32, device=device) if lists else None
-        self.q8 = torch.empty((B, N1, S, D), dtype=torch.uint8, device=device) if mix else None
-        self.k8 = torch.empty((B, N2, S, D), dtype=torch.uint8, device=device) if mix else None
-        self.q_scale = torch.empty((B, N1, nB), dtype=torch.float32, device=device) if mix else None
-        self.k_scale = torch.empty((B, N2, nB), dtype=torch.float32, device=device) if mix else None
         self.select_idx = (torch.empty((B * nB, N1, nB), dtype=torch.int32, device=device)
                            if lists else None)
         self.select_num = (torch.empty((B * nB, N1), dtype=torch.int32, device=device)

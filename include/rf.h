@@ -6,7 +6,7 @@
  * plan:
  *   rf_plan         host: validate a call, derive the arrangement and sizes
  *   rf_permute      arrange Q/K/V into 128-token space-time blocks, pool the
- *                   sparse blocks, and (mix, fp8 precision) quantise to fp8
+ *                   sparse blocks, and (mix, fp8, mxfp4 precision) quantise
  *   rf_pool_select  score pooled blocks and build selectIdx / selectNum
  *   rf_sparse_attn  exact softmax attention restricted to the listed blocks
  *   rf_dense_attn   the same attention over every block (the dense path)
@@ -25,7 +25,8 @@
  *          tokens, spatiotemporal permutation, first-frame sink).
  *   [MXA]  "MXAttention: Data-Free Optimal Scaling and Pre-Normalization
  *          Quantization for MXFP4 Attention" (catalyzex author page):
- *          abstract (softmax exponentials quantised before the row sum).
+ *          abstract (softmax exponentials quantised before the row sum; the
+ *          power-of-two scaling boundary 7.25 for MXFP4).
  *
  * Conventions for every entry point:
  *   - The caller owns all memory. Device pointers point to HIP device memory
@@ -82,7 +83,7 @@ typedef enum rf_precision {
   RF_PREC_MIX = 1,  /* Q/K as fp8 E4M3 with one fp32 scale per (batch, head, 128-row
                        block); V, probabilities and output bf16; fp32 softmax.
                        [RFA] Configuration names "mix" without defining it. */
-  RF_PREC_FP8 = 2   /* all operands E4M3. [RFA] Configuration names "fp8" without defining it.
+  RF_PREC_FP8 = 2,  /* all operands E4M3. [RFA] Configuration names "fp8" without defining it.
                        Q/K as in mix; V per (batch, kv head, 128-row block) with a
                        power-of-two scale 2^e, e the smallest integer with
                        amax <= 448 * 2^e (clamped to [-126, 127]; 0 for a zero block),
@@ -91,6 +92,21 @@ typedef enum rf_precision {
                        (128, 256]), and
                        out = sum P v / sum P (the sum of the rounded P; [MXA]).
                        Softmax bookkeeping and accumulation fp32, output bf16. */
+  RF_PREC_MXFP4 = 3 /* all operands OCP MXFP4: E2M1 values in blocks of 32 along each
+                       product's contraction, one E8M0 power-of-two scale 2^e per block.
+                       [RFA] Wan2.2 T2V quantization names "mxfp4" for the sparse operator;
+                       [MXA] gives the scale rule: e is the smallest integer with
+                       amax <= 7.25 * 2^e (clamped to [-127, 127]; -127 for a zero block),
+                       code = E2M1(x / 2^e), nearest-even, saturating at +-6. Blocks: 32
+                       channels of each Q and K row; for V and P the four 32-key quarters
+                       of each 128-row block (a short block's quarters hold its real rows).
+                       P = MXFP4 of 2^(t - M) with t and M as in fp8 (any integer M gives
+                       the same result), out = sum P v / sum P ([MXA]). No rotation
+                       ([RFA] mentions a default rotation policy without defining it).
+                       Softmax bookkeeping and accumulation fp32, output bf16.
+                       In this build rf_permute, rf_sparse_attn and rf_dense_attn return
+                       RF_ERR_UNSUPPORTED for it (its kernels are built but have not yet
+                       passed their check on the hardware); rf_plan reports its sizes. */
 } rf_precision;
 
 /* One attention call. Sizes are per batch item; all batch items share the
@@ -139,13 +155,23 @@ typedef struct rf_plan_info {
   int64_t k_scale_elems;    /* fp32 elements of k_scale (mix): batch*heads_kv*n_blocks */
   int64_t v_scale_elems;    /* fp32 elements of v_scale (fp8): batch*heads_kv*n_blocks */
   size_t ws_select_bytes;   /* workspace of rf_pool_select */
+  /* Bytes of the precision-dependent buffers for desc->precision (0 where the
+   * precision does not use the buffer):
+   *           bf16        mix            fp8            mxfp4
+   *   q8      0           qp_elems       qp_elems       qp_elems / 2
+   *   k8      0           kp_elems       kp_elems       kp_elems / 2
+   *   vpt     2*vpt_elems 2*vpt_elems    vpt_elems      vpt_elems / 2
+   *   q_scale 0           4*q_scale_elems 4*q_scale_elems batch*heads_q*seq_len*head_dim/32
+   *   k_scale 0           4*k_scale_elems 4*k_scale_elems batch*heads_kv*seq_len*head_dim/32
+   *   v_scale 0           0              4*v_scale_elems batch*heads_kv*n_blocks*4*head_dim */
+  int64_t q8_bytes, k8_bytes, vpt_bytes, q_scale_bytes, k_scale_bytes, v_scale_bytes;
 } rf_plan_info;
 
 /* Validate `desc` and derive the arrangement. Host only: touches no device,
  * so it can run on a machine without a GPU. */
 rf_status rf_plan(const rf_desc* desc, rf_plan_info* info);
 
-/* Step 1 (+ pooling, + fp8 quantisation). [RFA] introduction and Geometry
+/* Step 1 (+ pooling, + quantisation). [RFA] introduction and Geometry
  * handling; [XPR] commit summary (frame pairs, one call for Q, K and V);
  * [RF2] abstract (spatiotemporal permutation, block means).
  *
@@ -170,6 +196,17 @@ rf_status rf_plan(const rf_desc* desc, rf_plan_info* info);
  *   v_scale fp32 [B, N2, n_blocks] power-of-two V scales (fp8; required when v
  *          is given; ignored otherwise). In fp8 precision vpt holds one-byte
  *          E4M3 codes of V / v_scale in the same block-transposed layout.
+ * mxfp4 (RF_PREC_MXFP4; every buffer below required for a given input):
+ *   q8,k8   E2M1 codes, two per byte (channel 2i in the low nibble):
+ *           [B, N, S, D/2] bytes
+ *   q_scale,k_scale E8M0 exponents (e + 127) of each row's 32-channel blocks:
+ *           [B, N, S, D/32] bytes
+ *   vpt     E2M1 codes of V^T, two keys per byte (key 2i in the low nibble):
+ *           [B, N2, n_blocks, D, 64] bytes; keys past the block's end are 0
+ *   v_scale E8M0 exponents of V's key quarters: [B, N2, n_blocks, 4, D] bytes,
+ *           channel d = 32 a + i of quarter g at position (D/32) i + a of row
+ *           g (the order in which the attention kernel reads them)
+ * Sizes of every buffer: rf_plan_info (q8_bytes .. v_scale_bytes).
  * Mix quantisation of a block: amax = max |x|; r = 448.0f / amax;
  * code = E4M3 round-to-nearest-even, saturating at 448, of (float)(x * r);
  * scale = amax / 448.0f; an all-zero block gets r = scale = 1.
@@ -178,7 +215,7 @@ rf_status rf_plan(const rf_desc* desc, rf_plan_info* info);
  * input), plus the descriptor errors of rf_plan. */
 rf_status rf_permute(const rf_desc* desc, const void* q, const void* k, const void* v,
                      void* qp, void* kp, void* vpt, float* q_pool, float* k_pool,
-                     uint8_t* q8, uint8_t* k8, float* q_scale, float* k_scale, float* v_scale,
+                     uint8_t* q8, uint8_t* k8, void* q_scale, void* k_scale, void* v_scale,
                      void* stream);
 
 /* Steps 2-3. [RFA] introduction (pool 128-token blocks, rank per query
@@ -208,15 +245,18 @@ rf_status rf_pool_select(const rf_desc* desc, const void* qp, const void* kp,
  * bf16 precision reads qp, kp, vpt; mix precision reads q8, k8, q_scale,
  * k_scale, vpt (logits = scale * q_scale * k_scale * <q8, k8>); fp8 precision
  * also reads v_scale, with vpt as E4M3 codes, and quantises P (see
- * RF_PREC_FP8). Arguments a precision does not read may be NULL.
+ * RF_PREC_FP8); mxfp4 reads q8, k8, q_scale, k_scale, vpt and v_scale in the
+ * layouts rf_permute writes for it and quantises P (see RF_PREC_MXFP4).
+ * Scale arguments are fp32 arrays (mix, fp8) or E8M0 byte arrays (mxfp4).
+ * Arguments a precision does not read may be NULL.
  * select_idx / select_num as above (any list the caller builds is accepted:
  * entries outside [0, n_blocks) contribute nothing, exactly as if skipped,
  * provided V holds finite values; counts are clamped to max_kv).
  * A row with an empty list gets zeros.
  * out_p: bf16 [B, N1, S, D], permuted row order, rounded to nearest even. */
 rf_status rf_sparse_attn(const rf_desc* desc, const void* qp, const void* kp, const void* vpt,
-                         const uint8_t* q8, const uint8_t* k8, const float* q_scale,
-                         const float* k_scale, const float* v_scale, const int32_t* select_idx,
+                         const uint8_t* q8, const uint8_t* k8, const void* q_scale,
+                         const void* k_scale, const void* v_scale, const int32_t* select_idx,
                          const int32_t* select_num, int32_t max_kv, void* out_p, void* stream);
 
 /* Dense path. [RFA] introduction: calls that RainFusion does not handle, and
@@ -230,8 +270,8 @@ rf_status rf_sparse_attn(const rf_desc* desc, const void* qp, const void* kp, co
  * Arguments, layouts and errors as rf_sparse_attn without the lists.
  * out_p: bf16 [B, N1, S, D], permuted row order, rounded to nearest even. */
 rf_status rf_dense_attn(const rf_desc* desc, const void* qp, const void* kp, const void* vpt,
-                        const uint8_t* q8, const uint8_t* k8, const float* q_scale,
-                        const float* k_scale, const float* v_scale, void* out_p, void* stream);
+                        const uint8_t* q8, const uint8_t* k8, const void* q_scale,
+                        const void* k_scale, const void* v_scale, void* out_p, void* stream);
 
 /* Step 5. [XPR] commit summary (inverse rearrange; roundtrip check).
  * out[natural row pi(r)] = out_p[r]; out in the caller's layout with heads_q

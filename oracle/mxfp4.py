@@ -58,16 +58,15 @@ def e2m1_decode(codes: np.ndarray) -> np.ndarray:
 def e2m1_encode(x: np.ndarray) -> np.ndarray:
     """Finite values -> uint8 E2M1 codes: nearest, ties to even, saturating at +-6.
 
-    In the binade [2**j, 2**(j+1)) (j >= 0; the subnormal range [0, 1) joins
-    j = 0) the quantum is 2**(j-1); the magnitude is rounded to a whole number
-    of quanta (halves to even, which is the even code), then capped at 6."""
+    The spacing of the values is 0.5 below 2 (the subnormals 0, 0.5 and the
+    binade [1, 2)), 1 in [2, 4) and 2 from 4 on; the magnitude is rounded to a
+    whole number of that quantum (halves to even, which is the even code),
+    then capped at 6."""
     x = np.asarray(x, dtype=np.float64)
     if not np.all(np.isfinite(x)):
         raise ValueError("e2m1_encode takes finite values only")
     a = np.abs(x)
-    _, ex = np.frexp(np.where(a > 0, a, 1.0))         # a = f * 2**ex, f in [0.5, 1)
-    j = np.clip(ex - 1, 0, 2)                          # binade exponent, 0 for a < 2
-    quantum = np.exp2(j - 1.0)
+    quantum = np.where(a < 2.0, 0.5, np.where(a < 4.0, 1.0, 2.0))
     val = np.minimum(np.round(a / quantum) * quantum, E2M1_MAX)
     mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
     code = np.searchsorted(mags, val)                  # val is exactly one of mags

@@ -62,6 +62,9 @@ WORKLOADS = {
     # The Wan2.2 shapes and data with every attention operand in fp8 e4m3 ("fp8").
     "wan22_fp8": Workload("wan22_fp8", 1, 40, 40, 128, 512, (21, 40, 64), True, 0.8, "fp8", True,
                           1002),
+    # The Wan2.2 shapes and data with every attention operand in MXFP4 ("mxfp4").
+    "wan22_mxfp4": Workload("wan22_mxfp4", 1, 40, 40, 128, 512, (21, 40, 64), True, 0.8, "mxfp4",
+                            True, 1002),
     # Long video with grouped-query attention: 8 query heads share 2 KV heads.
     "gqa_long": Workload("gqa_long", 1, 8, 2, 128, 512, (31, 64, 96), True, 0.9, "bf16", True, 1005),
 }

@@ -33,6 +33,21 @@ import oracle
 from oracle.geometry import Geometry
 from synth import bf16_to_f32
 
+MXFP4_TOL = (0.25, 2e-3)
+# The library refuses mxfp4 in its device entry points for now (RF_ERR_UNSUPPORTED):
+# the mxfp4 attention kernel faulted the GPU on its first runs (it read the fp8
+# block scale through a pointer that is unset in mxfp4; fixed on the CPU side,
+# shown in the compiled code), and the fixed kernels have not had their check on
+# the hardware yet.
+MXFP4_SKIP = ("mxfp4 kernels switched off: they faulted the GPU on their first runs (null fp8 "
+              "block-scale pointer read in mxfp4, since fixed); re-enabled after the fix passes "
+              "its hardware check")
+
+
+def mx_param(name):
+    """A parametrize value, skipped (with the reason) if it runs the mxfp4 kernels."""
+    import pytest
+    return pytest.param(name, marks=pytest.mark.skip(reason=MXFP4_SKIP)) if "mxfp4" in name else name
 BF16_TOL = (2e-2, 2e-3)
 MIX_TOL = (6e-2, 6e-3)
 FP8_TOL = (6e-2, 2e-3)
@@ -83,6 +98,28 @@ def expected_vpt(vp_u16, p, D):
     return out
 
 
+def unpack_e2m1(packed):
+    """Bytes holding two E2M1 codes (element 2i in the low nibble) -> one code
+    per element along the last axis."""
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 0xF
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def mx_v_scale_natural(v_scale):
+    """Kernel-order V scale bytes ``[B, N, nB, 4, D]`` (channel 32 a + i at
+    position (D/32) i + a) -> natural channel order."""
+    v = np.asarray(v_scale)
+    D = v.shape[-1]
+    DT = D // 32
+    a, i = np.meshgrid(np.arange(DT), np.arange(32), indexing="ij")
+    out = np.empty_like(v)
+    out[..., (32 * a + i).ravel()] = v[..., (DT * i + a).ravel()]
+    return out
+
+
 def check_selection(p, batch, heads_q, gpu_idx, gpu_num, scores, max_kv=None):
     """Compare GPU selectIdx/selectNum with the oracle's rule (near-ties allowed)."""
     nB = p.n_blocks
@@ -116,6 +153,18 @@ def check_selection(p, batch, heads_q, gpu_idx, gpu_num, scores, max_kv=None):
 def attention_error(gpu_out_f32, ref):
     err = np.abs(gpu_out_f32.astype(np.float64) - ref)
     return float(err.max()), float(err.mean())
+
+
+def assert_close_mx(gpu_out_f32, ref, tol, what="", frac_max=5e-3):
+    """mxfp4: max-abs and mean-abs as assert_close, and at most ``frac_max`` of
+    the elements outside the bf16 max-abs bound (a P code that flips at an E2M1
+    rounding midpoint moves its row; all other rows match to bf16 rounding)."""
+    err = np.abs(gpu_out_f32.astype(np.float64) - ref)
+    mx, mean = float(err.max()), float(err.mean())
+    frac = float((err > BF16_TOL[0]).mean())
+    log(f"  {what} max-abs {mx:.3e} mean-abs {mean:.3e} beyond-bf16 {frac:.2e} "
+        f"(tol {tol[0]:.0e}/{tol[1]:.0e}/{frac_max:.0e})")
+    assert mx <= tol[0] and mean <= tol[1] and frac <= frac_max, (what, mx, mean, frac)
 
 
 def assert_close(gpu_out_f32, ref, tol, what=""):

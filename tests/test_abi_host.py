@@ -140,6 +140,34 @@ def test_invalid_descriptors(name, change, status):
     assert lib.rf_unpermute(ctypes.byref(c), fake, fake, None) == status
 
 
+def test_mxfp4_sizes_planned_and_device_entry_points_refused():
+    """rf_plan reports the mxfp4 buffer sizes; the device entry points refuse the
+    precision (RF_ERR_UNSUPPORTED) before any launch while its kernels are off."""
+    d = _good()
+    d.precision = "mxfp4"
+    info = rf.rf_plan(d)
+    B, N1, N2, S, D = d.batch, d.heads_q, d.heads_kv, d.seq_len, d.head_dim
+    assert info.q8_bytes == B * N1 * S * D // 2 and info.k8_bytes == B * N2 * S * D // 2
+    assert info.q_scale_bytes == B * N1 * S * D // 32 and info.k_scale_bytes == B * N2 * S * D // 32
+    assert info.vpt_bytes == B * N2 * info.n_blocks * D * 64
+    assert info.v_scale_bytes == B * N2 * info.n_blocks * 4 * D
+    lib = load_library()
+    c = d.c()
+    fake = ctypes.c_void_p(1 << 40)
+    assert lib.rf_permute(ctypes.byref(c), fake, None, None, None, None, None, None, None,
+                          ctypes.c_void_p(2 << 40), None, ctypes.c_void_p(3 << 40), None, None,
+                          None) == 10
+    assert lib.rf_sparse_attn(ctypes.byref(c), None, None, fake, fake, fake, fake, fake, fake,
+                              fake, fake, info.n_blocks, ctypes.c_void_p(5 << 40), None) == 10
+    assert lib.rf_dense_attn(ctypes.byref(c), None, None, fake, fake, fake, fake, fake, fake,
+                             ctypes.c_void_p(5 << 40), None) == 10
+    # Per-precision sizes of the other modes.
+    for prec, q8, vpt in (("bf16", 0, 2), ("mix", 1, 2), ("fp8", 1, 1)):
+        d.precision = prec
+        i = rf.rf_plan(d)
+        assert i.q8_bytes == q8 * i.qp_elems and i.vpt_bytes == vpt * i.vpt_elems
+
+
 def test_status_strings():
     for s in range(14):
         assert rf.rf_status_str(s) and rf.rf_status_str(s) != "unknown status"

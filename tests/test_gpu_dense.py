@@ -13,7 +13,8 @@ import pytest
 import oracle
 from synth import WORKLOADS, Workload, make_qkv, to_tnd, from_tnd
 
-from gpu_harness import (BF16_TOL, FP8_E2E_TOL, MIX_TOL, assert_close, f32, log, to_dev,
+from gpu_harness import (BF16_TOL, FP8_E2E_TOL, MIX_TOL, MXFP4_TOL, assert_close_mx, assert_close,
+                         mx_param, f32, log, to_dev,
                          to_host_u16)
 
 pytestmark = pytest.mark.gpu
@@ -29,6 +30,9 @@ CASES = {
     "tiny_fp8": (WORKLOADS["tiny"].with_(precision="fp8"), "BNSD"),
     "ragged_gqa_fp8": (_custom("ragged_gqa", 1, 4, 2, 128, 200, (10, 17, 34), True, 0.8, "fp8"),
                        "BNSD"),
+    "tiny_mxfp4": (WORKLOADS["tiny"].with_(precision="mxfp4"), "BNSD"),
+    "ragged_gqa_mxfp4": (_custom("ragged_gqa", 1, 4, 2, 128, 200, (10, 17, 34), True, 0.8,
+                                 "mxfp4"), "BNSD"),
     "tiny_tnd_b2": (WORKLOADS["tiny"].with_(batch=2), "TND"),
     "ragged_gqa": (_custom("ragged_gqa", 1, 4, 2, 128, 200, (10, 17, 34), True, 0.8), "BNSD"),
     "minimax_small": (_custom("minimax_small", 1, 2, 2, 128, 512, (6, 24, 42), False, 0.8),
@@ -49,7 +53,7 @@ def _full_attention(q, k, v, scale):
     return out
 
 
-@pytest.mark.parametrize("name", sorted(CASES))
+@pytest.mark.parametrize("name", [mx_param(n) for n in sorted(CASES)])
 def test_dense_path_equals_full_attention(name):
     import torch
     import block_sparse_video_rf_amd as rf
@@ -65,12 +69,27 @@ def test_dense_path_equals_full_attention(name):
     got = to_host_u16(out)
     if layout == "TND":
         got = from_tnd(got, w.batch)
+    if w.precision == "mxfp4":
+        # MXFP4 groups V and P by the quarters of the arranged blocks, so the
+        # reference is the oracle's mxfp4 attention with every block listed
+        # in that arrangement (the same quantised operands).
+        from gpu_harness import geometry_of
+        from oracle.geometry import plan
+        p = plan(geometry_of(desc))
+        nB = p.n_blocks
+        idx = np.tile(np.arange(nB, dtype=np.int32), (w.batch * nB, w.heads_q, 1))
+        num = np.full((w.batch * nB, w.heads_q), nB, dtype=np.int32)
+        ref = oracle.run(f32(q), f32(k), f32(v), geometry_of(desc), precision="mxfp4",
+                         select=(idx, num), batch=w.batch)["out"]
+        assert_close_mx(f32(got), ref, MXFP4_TOL, f"dense {name}")
+        return
     ref = _full_attention(f32(q), f32(k), f32(v), 1.0 / np.sqrt(w.head_dim))
     tol = {"bf16": BF16_TOL, "mix": MIX_TOL, "fp8": FP8_E2E_TOL}[w.precision]
     assert_close(f32(got), ref, tol, f"dense {name}")
 
 
-@pytest.mark.parametrize("name", ["ragged_gqa", "tiny_mix", "ragged_gqa_fp8"])
+@pytest.mark.parametrize("name", [mx_param(n) for n in ("ragged_gqa", "tiny_mix", "ragged_gqa_fp8",
+                                                        "ragged_gqa_mxfp4")])
 def test_dense_entry_point_equals_sparse_kernel_with_every_block(name):
     import torch
     import block_sparse_video_rf_amd as rf

@@ -15,7 +15,8 @@ import oracle
 from oracle.geometry import plan, permutation
 from synth import WORKLOADS, make_qkv
 
-from gpu_harness import (BF16_TOL, FP8_E2E_TOL, FP8_TOL, MIX_TOL, assert_close, check_selection,
+from gpu_harness import (BF16_TOL, FP8_E2E_TOL, FP8_TOL, MIX_TOL, MXFP4_TOL, mx_v_scale_natural,
+                         unpack_e2m1, mx_param, assert_close, check_selection,
                          expected_vpt, f32, geometry_of, log, run_gpu, to_host_u16)
 
 pytestmark = pytest.mark.gpu
@@ -32,7 +33,8 @@ def _samples(p, heads, rng, n_sparse=24):
     return sorted(set(picks))
 
 
-@pytest.mark.parametrize("name", ["wan22", "minimax_h3", "wan22_mix", "wan22_fp8", "gqa_long"])
+@pytest.mark.parametrize("name", [mx_param(n) for n in ("wan22", "minimax_h3", "wan22_mix",
+                                                        "wan22_fp8", "wan22_mxfp4", "gqa_long")])
 def test_full_size(name):
     import block_sparse_video_rf_amd as rf
     w = WORKLOADS[name]
@@ -55,6 +57,11 @@ def test_full_size(name):
         v8, sv = oracle.quantize_blocks_pow2(f32(vp_o), p)
         assert np.array_equal(bufs.vpt.cpu().numpy(), expected_vpt(v8, p, w.head_dim))
         assert np.array_equal(bufs.v_scale.cpu().numpy(), sv)
+    elif w.precision == "mxfp4":
+        v4, ev = oracle.quantize_v_mx(f32(vp_o), p)
+        assert np.array_equal(unpack_e2m1(bufs.vpt.cpu().numpy()), expected_vpt(v4, p, w.head_dim))
+        assert np.array_equal(mx_v_scale_natural(bufs.v_scale.cpu().numpy()),
+                              (ev + 127).astype(np.uint8))
     else:
         assert np.array_equal(to_host_u16(bufs.vpt), expected_vpt(vp_o, p, w.head_dim))
     log("  permute bit-exact")
@@ -78,6 +85,18 @@ def test_full_size(name):
         assert np.array_equal(bufs.q_scale.cpu().numpy(), sq)
         assert np.array_equal(bufs.k_scale.cpu().numpy(), sk)
         log("  fp8 codes and scales bit-exact")
+    if w.precision == "mxfp4":
+        q4, eq = oracle.quantize_rows_mx(q_att)
+        k4, ek = oracle.quantize_rows_mx(k_att)
+        assert np.array_equal(unpack_e2m1(bufs.q8.cpu().numpy()), q4)
+        assert np.array_equal(unpack_e2m1(bufs.k8.cpu().numpy()), k4)
+        assert np.array_equal(bufs.q_scale.cpu().numpy(), (eq + 127).astype(np.uint8))
+        assert np.array_equal(bufs.k_scale.cpu().numpy(), (ek + 127).astype(np.uint8))
+        log("  mxfp4 codes and scales bit-exact")
+        qdq = oracle.dequantize_rows_mx(q4, eq)
+        kdq = oracle.dequantize_rows_mx(k4, ek)
+        vdq = oracle.dequantize_v_mx(v4, ev, p)
+        errs_same, errs_own, errs_dev = [], [], []
     rng = np.random.default_rng(11)
     picks = _samples(p, w.heads_q, rng)
     out_nat = f32(to_host_u16(res["out"]))
@@ -89,6 +108,17 @@ def test_full_size(name):
         ids = gi[qb, n, :gn[qb, n]]
         rows = oracle.attention.listed_rows(p, ids)
         refs = []
+        if w.precision == "mxfp4":
+            got = out_nat[b, n, pi[r0:r0 + m]].astype(np.float64)
+            ref = oracle.attention_block_mxp(qdq[b, n, r0:r0 + m], kdq[b, n // G, rows],
+                                             vdq[b, n // G, rows], scale,
+                                             oracle.attention.listed_groups(p, ids))
+            exact = oracle.attention_block(q_att[b, n, r0:r0 + m], k_att[b, n // G, rows],
+                                           vp_f[b, n // G, rows], scale)
+            errs_same.append(np.abs(got - ref).ravel())
+            errs_own.append(np.abs(ref - exact).ravel())
+            errs_dev.append(np.abs(got - exact).ravel())
+            continue
         if w.precision in ("mix", "fp8"):
             def deq(codes, sig):
                 return np.concatenate([oracle.e4m3_decode(codes[b, n // G, p.blocks[j][0]:
@@ -113,5 +143,18 @@ def test_full_size(name):
             err = np.abs(got.astype(np.float64) - ref)
             assert err.max() <= tol[0] and err.mean() <= tol[1], (b, qb, n, err.max(), err.mean())
             worst = [max(worst[0], err.max()), max(worst[1], err.mean())]
+    if w.precision == "mxfp4":
+        # Over all sampled blocks: the mxfp4 bound against the oracle's reading
+        # on the same codes, and end to end no further from the unquantised
+        # result than the oracle's own mxfp4 output is.
+        e_same = np.concatenate(errs_same)
+        frac = float((e_same > BF16_TOL[0]).mean())
+        own, dev = np.concatenate(errs_own), np.concatenate(errs_dev)
+        log(f"  attention on {len(picks)} sampled blocks: max-abs {e_same.max():.3e} mean-abs "
+            f"{e_same.mean():.3e} beyond-bf16 {frac:.2e}; end to end mean {dev.mean():.3e} "
+            f"(oracle mxfp4 {own.mean():.3e})")
+        assert e_same.max() <= MXFP4_TOL[0] and e_same.mean() <= MXFP4_TOL[1] and frac <= 5e-3
+        assert dev.mean() <= 1.05 * own.mean() + 1e-4
+        return
     log(f"  attention on {len(picks)} sampled blocks: worst max-abs {worst[0]:.3e} "
         f"mean-abs {worst[1]:.3e}")

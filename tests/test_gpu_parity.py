@@ -16,8 +16,9 @@ import oracle
 from oracle.geometry import plan, permutation
 from synth import WORKLOADS, Workload, make_qkv, to_tnd, from_tnd
 
-from gpu_harness import (BF16_TOL, FP8_E2E_TOL, FP8_TOL, MIX_TOL, assert_close, check_selection,
-                         expected_vpt, f32, geometry_of, log, run_gpu, to_host_u16)
+from gpu_harness import (BF16_TOL, FP8_E2E_TOL, FP8_TOL, MIX_TOL, MXFP4_TOL, assert_close,
+                         assert_close_mx, check_selection, expected_vpt, f32, geometry_of, log,
+                         mx_param, mx_v_scale_natural, run_gpu, to_host_u16, unpack_e2m1)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,6 +52,12 @@ SMALL = {
                                precision="fp8"), {}),
     "minimax_small_fp8_tnd_b2": (_custom("minimax_small", 2, 2, 2, 128, 512, (6, 24, 42), False,
                                          0.8, precision="fp8"), {"layout": "TND"}),
+    # mxfp4 precision: D=64; ragged GQA D=128; a 32-row last block in TND with batch 2
+    "tiny_mxfp4": (WORKLOADS["tiny"].with_(precision="mxfp4"), {}),
+    "ragged_gqa_mxfp4": (_custom("ragged_gqa", 1, 4, 2, 128, 200, (10, 17, 34), True, 0.8,
+                                 precision="mxfp4"), {}),
+    "minimax_small_mxfp4_tnd_b2": (_custom("minimax_small", 2, 2, 2, 128, 512, (6, 24, 42), False,
+                                           0.8, precision="mxfp4"), {"layout": "TND"}),
     # no geometry at all: dense over a sequence that is not a multiple of 128
     "no_grid": (_custom("no_grid", 1, 2, 2, 128, 1000, (0, 0, 0), False, 0.8), {"grid": (0, 0, 0)}),
 }
@@ -104,6 +111,11 @@ def _full_check(name):
         vpt = bufs.vpt.cpu().numpy()
         assert np.array_equal(vpt, expected_vpt(ores["v8"], p, w.head_dim))
         assert np.array_equal(bufs.v_scale.cpu().numpy(), ores["v_scale"])
+    elif w.precision == "mxfp4":
+        vpt = unpack_e2m1(bufs.vpt.cpu().numpy())
+        assert np.array_equal(vpt, expected_vpt(ores["v4"], p, w.head_dim))
+        assert np.array_equal(mx_v_scale_natural(bufs.v_scale.cpu().numpy()),
+                              (ores["v_exp"] + 127).astype(np.uint8))
     else:
         vpt = to_host_u16(bufs.vpt)
         assert np.array_equal(vpt, expected_vpt(oracle.permute_rows(vb, pi), p, w.head_dim))
@@ -113,8 +125,13 @@ def _full_check(name):
         kpool = bufs.k_pool.cpu().numpy()
         assert np.abs(qpool - ores["q_pool"]).max() <= 2e-6
         assert np.abs(kpool - ores["k_pool"]).max() <= 2e-6
-    # Mix and fp8: codes and scales, bit for bit.
-    if w.precision in ("mix", "fp8"):
+    # Quantised Q/K: codes and scales, bit for bit.
+    if w.precision == "mxfp4":
+        assert np.array_equal(unpack_e2m1(bufs.q8.cpu().numpy()), ores["q4"])
+        assert np.array_equal(unpack_e2m1(bufs.k8.cpu().numpy()), ores["k4"])
+        assert np.array_equal(bufs.q_scale.cpu().numpy(), (ores["q_exp"] + 127).astype(np.uint8))
+        assert np.array_equal(bufs.k_scale.cpu().numpy(), (ores["k_exp"] + 127).astype(np.uint8))
+    elif w.precision in ("mix", "fp8"):
         assert np.array_equal(bufs.q8.cpu().numpy(), ores["q8"])
         assert np.array_equal(bufs.k8.cpu().numpy(), ores["k8"])
         assert np.array_equal(bufs.q_scale.cpu().numpy(), ores["q_scale"])
@@ -128,12 +145,23 @@ def _full_check(name):
     out = f32(to_host_u16(res["out"]))
     ref_same_sel = oracle.run(f32(q), f32(k), f32(v), g, precision=w.precision, layout=layout,
                               batch=w.batch, select=(gi, gn))["out"]
-    assert_close(out, ref_same_sel, FP8_TOL if w.precision == "fp8" else BF16_TOL,
-                 "attention (GPU lists)")
-    tol = {"bf16": BF16_TOL, "mix": MIX_TOL, "fp8": FP8_E2E_TOL}[w.precision]
     bf16_ref = ores["out"] if w.precision == "bf16" else oracle.run(
         f32(q), f32(k), f32(v), g, layout=layout, batch=w.batch)["out"]
-    assert_close(out, bf16_ref, tol, "end to end vs bf16 oracle")
+    if w.precision == "mxfp4":
+        assert_close_mx(out, ref_same_sel, MXFP4_TOL, "attention (GPU lists)")
+        # End to end: MXFP4 is coarse, so the bar is the oracle's own mxfp4
+        # deviation from the unquantised result on the same inputs.
+        own = np.abs(ores["out"] - bf16_ref)
+        dev = np.abs(out.astype(np.float64) - bf16_ref)
+        log(f"  end to end vs bf16 oracle: mean-abs {dev.mean():.3e} (oracle mxfp4 {own.mean():.3e}), "
+            f"max-abs {dev.max():.3e} (oracle {own.max():.3e})")
+        assert dev.mean() <= 1.05 * own.mean() + 1e-4
+        assert dev.max() <= own.max() + MXFP4_TOL[0]
+    else:
+        assert_close(out, ref_same_sel, FP8_TOL if w.precision == "fp8" else BF16_TOL,
+                     "attention (GPU lists)")
+        tol = {"bf16": BF16_TOL, "mix": MIX_TOL, "fp8": FP8_E2E_TOL}[w.precision]
+        assert_close(out, bf16_ref, tol, "end to end vs bf16 oracle")
     # Roundtrip: the inverse arrangement of the permuted Q is Q itself.
     if bufs.qp is not None:
         import torch
@@ -145,7 +173,7 @@ def _full_check(name):
     return res, ores
 
 
-@pytest.mark.parametrize("name", sorted(SMALL))
+@pytest.mark.parametrize("name", [mx_param(n) for n in sorted(SMALL)])
 def test_small_case(name):
     _full_check(name)
 
@@ -164,7 +192,7 @@ def test_dense_cases_equal_dense_attention():
         assert_close(f32(to_host_u16(res["out"])), ref, BF16_TOL, f"{name} vs torch SDPA")
 
 
-@pytest.mark.parametrize("precision", ["bf16", "mix", "fp8"])
+@pytest.mark.parametrize("precision", [mx_param(x) for x in ("bf16", "mix", "fp8", "mxfp4")])
 def test_empty_lists_give_zeros(precision):
     """Sparsity 1, no prefix, no first frame, aligned grid: every list is empty."""
     w = _custom("empty", 1, 2, 2, 128, 0, (4, 16, 16), False, 1.0, precision=precision)
@@ -176,7 +204,7 @@ def test_empty_lists_give_zeros(precision):
     assert np.all(to_host_u16(res["out"]) == 0)
 
 
-@pytest.mark.parametrize("precision", ["bf16", "mix", "fp8"])
+@pytest.mark.parametrize("precision", [mx_param(x) for x in ("bf16", "mix", "fp8", "mxfp4")])
 def test_handmade_lists_skip_invalid_entries(precision):
     """rf_sparse_attn accepts any list: -1 and out-of-range ids are skipped, counts clamped."""
     import torch
@@ -212,8 +240,11 @@ def test_handmade_lists_skip_invalid_entries(precision):
     # The oracle on the valid entries only, with the precision's own quantisation.
     ref = oracle.run(f32(q), f32(k), f32(v), g, precision=precision,
                      select=(valid_idx, valid_num))["out_p"]
-    assert_close(f32(to_host_u16(out_p)), ref, FP8_TOL if precision == "fp8" else BF16_TOL,
-                 f"handmade lists ({precision})")
+    if precision == "mxfp4":
+        assert_close_mx(f32(to_host_u16(out_p)), ref, MXFP4_TOL, "handmade lists (mxfp4)")
+    else:
+        assert_close(f32(to_host_u16(out_p)), ref, FP8_TOL if precision == "fp8" else BF16_TOL,
+                     f"handmade lists ({precision})")
 
 
 def test_recomputed_pools_and_determinism():
@@ -265,7 +296,7 @@ def test_selection_paths_by_sparse_count(grid):
     log(f"  selection exact ({swaps} near-tie rows)")
 
 
-@pytest.mark.parametrize("precision", ["bf16", "mix", "fp8"])
+@pytest.mark.parametrize("precision", [mx_param(x) for x in ("bf16", "mix", "fp8", "mxfp4")])
 def test_reference_raised_mid_row(precision):
     """Keys in the second half of the sequence scaled by 100: their logits exceed
     the reference the first blocks set by far more than 2^64 allows, so the
@@ -289,5 +320,9 @@ def test_reference_raised_mid_row(precision):
     # rounds to the neighbouring E4M3 code (fp32 against float64 logits at a
     # rounding midpoint) moves a two-key row by w (1 - w) / 8 * |v1 - v2|, at
     # most 0.25. A wrong rescale would show in the mean, which keeps its bound.
+    if precision == "mxfp4":
+        assert_close_mx(f32(to_host_u16(res["out"])), ref, MXFP4_TOL, "raised mid-row (mxfp4)",
+                        frac_max=2e-2)
+        return
     tol = (0.25, FP8_TOL[1]) if precision == "fp8" else (4e-2, BF16_TOL[1])
     assert_close(f32(to_host_u16(res["out"])), ref, tol, f"raised mid-row ({precision})")

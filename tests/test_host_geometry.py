@@ -23,16 +23,16 @@ def dump_exe(tmp_path_factory):
     with open(stub, "w") as f:
         f.write('#include "rf_internal.h"\n'
                 'rf_status rf_launch_permute(const RfGeom&, int32_t, const void*, const void*, '
-                'const void*, void*, void*, void*, float*, float*, uint8_t*, uint8_t*, float*, '
-                'float*, float*, void*) { return RF_ERR_HIP; }\n'
+                'const void*, void*, void*, void*, float*, float*, uint8_t*, uint8_t*, void*, '
+                'void*, void*, void*) { return RF_ERR_HIP; }\n'
                 'rf_status rf_launch_unpermute(const RfGeom&, const void*, void*, void*) '
                 '{ return RF_ERR_HIP; }\n'
                 'rf_status rf_launch_pool_select(const RfGeom&, float, const void*, const void*, '
                 'const float*, const float*, int32_t*, int32_t*, int32_t, void*, void*) '
                 '{ return RF_ERR_HIP; }\n'
                 'rf_status rf_launch_sparse_attn(const RfGeom&, int32_t, float, const void*, '
-                'const void*, const void*, const uint8_t*, const uint8_t*, const float*, '
-                'const float*, const float*, const int32_t*, const int32_t*, int32_t, void*, '
+                'const void*, const void*, const uint8_t*, const uint8_t*, const void*, '
+                'const void*, const void*, const int32_t*, const int32_t*, int32_t, void*, '
                 'void*) '
                 '{ return RF_ERR_HIP; }\n')
     subprocess.run(["g++", "-O1", "-std=c++17", "-fsanitize=address,undefined",

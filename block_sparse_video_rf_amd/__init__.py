@@ -6,9 +6,9 @@ The compute lives in the HIP library ``librf.so`` (C ABI in ``include/rf.h``);
 from .rf import (Buffers, Desc, RfError, RfPlanInfo, attention, dense_attention, load_library,
                  rf_dense_attn, rf_permute, rf_plan, rf_pool_select, rf_sparse_attn,
                  rf_status_str, rf_unpermute, rf_version, EXPORTS, LIB_PATH)
-from .schedule import DenseSchedule, parse_layers, scheduled_attention
+from .schedule import DenseSchedule, QuantSkips, parse_layers, route, scheduled_attention
 
-__all__ = ["Buffers", "DenseSchedule", "Desc", "RfError", "RfPlanInfo", "attention",
+__all__ = ["Buffers", "DenseSchedule", "QuantSkips", "route", "Desc", "RfError", "RfPlanInfo", "attention",
            "dense_attention", "load_library", "parse_layers", "rf_dense_attn", "rf_permute",
            "rf_plan", "rf_pool_select", "rf_sparse_attn", "rf_status_str", "rf_unpermute",
            "rf_version", "scheduled_attention", "EXPORTS", "LIB_PATH"]

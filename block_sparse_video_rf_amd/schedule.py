@@ -9,11 +9,19 @@ library's ``rf_dense_attn``). The same introduction sends calls without a
 usable video geometry (no grid, fewer than 32 sparse blocks, sparsity 0) to
 full attention too: ``rf_plan`` reports those as ``dense_fallback``, and
 ``scheduled_attention`` routes them to the dense path whatever the schedule.
+
+The same page's "Wan2.2 T2V quantization" section adds, for the quantised
+precisions, ``diffusion_kv_cache_skip_steps`` and ``..._skip_layers``: the
+forwards they name run floating-point block-sparse attention (bf16 here) and
+stay sparse, while the warm-up steps and layer exclusions above still select
+dense attention in the configured (shared) precision. Its step indices are
+fixed: they do not follow a changed step count. ``route`` states the rule.
 """
 from __future__ import annotations
 
+import dataclasses
 from dataclasses import dataclass, field
-from typing import FrozenSet
+from typing import FrozenSet, Optional, Tuple
 
 
 def parse_layers(selector) -> FrozenSet[int]:
@@ -78,15 +86,53 @@ class DenseSchedule:
         return layer not in self.skip_layers
 
 
+@dataclass(frozen=True)
+class QuantSkips:
+    """``diffusion_kv_cache_skip_steps`` / ``..._skip_layers``: the denoise steps
+    (fixed 0-based indices) and DiT layers whose sparse attention runs in
+    floating point when the configured precision is quantised. Selectors as
+    ``parse_layers`` (the page recommends ``"0,1,38,39"`` and ``"0,39"`` for 40
+    steps)."""
+
+    skip_steps: FrozenSet[int] = field(default_factory=frozenset)
+    skip_layers: FrozenSet[int] = field(default_factory=frozenset)
+
+    def __post_init__(self):
+        object.__setattr__(self, "skip_steps", parse_layers(self.skip_steps))
+        object.__setattr__(self, "skip_layers", parse_layers(self.skip_layers))
+
+    def floating(self, step: int, layer: int) -> bool:
+        return step in self.skip_steps or layer in self.skip_layers
+
+
+def route(schedule: DenseSchedule, quant_skips: Optional[QuantSkips], precision: str, step: int,
+          num_steps: int, layer: int) -> Tuple[str, str]:
+    """``("sparse" | "dense", precision)`` of one forward. The dense schedule
+    decides the path first; dense forwards keep the configured precision (the
+    page shares it between the dense and sparse paths). Of the sparse forwards
+    of a quantised precision, those the skips name run in bf16."""
+    if not schedule.sparse(step, num_steps, layer):
+        return "dense", precision
+    if precision != "bf16" and quant_skips is not None and quant_skips.floating(step, layer):
+        return "sparse", "bf16"
+    return "sparse", precision
+
+
 def scheduled_attention(q, k, v, desc, schedule: DenseSchedule, step: int, num_steps: int,
-                        layer: int, bufs=None, out=None, stream=None):
+                        layer: int, bufs=None, out=None, stream=None,
+                        quant_skips: Optional[QuantSkips] = None):
     """``attention`` on the steps and layers the schedule makes sparse,
-    ``dense_attention`` on the others and on geometry fallbacks. Returns
-    (out, bufs, sparse?)."""
+    ``dense_attention`` on the others and on geometry fallbacks; with
+    ``quant_skips``, the named sparse forwards of a quantised precision run in
+    bf16. Returns (out, bufs, sparse?); ``bufs`` are the buffers of the
+    precision that ran (reused when they match the next call's)."""
     from .rf import Buffers, attention, dense_attention
-    if bufs is None:  # buffers that serve both paths, for reuse across calls
+    path, prec = route(schedule, quant_skips, desc.precision, step, num_steps, layer)
+    if prec != desc.precision:
+        desc = dataclasses.replace(desc, precision=prec)
+    if bufs is None or bufs.desc != desc:  # buffers that serve both paths of this precision
         bufs = Buffers(desc, device=q.device, lists=True)
-    if schedule.sparse(step, num_steps, layer) and not bufs.info.dense_fallback:
+    if path == "sparse" and not bufs.info.dense_fallback:
         out, bufs = attention(q, k, v, desc, bufs=bufs, out=out, stream=stream)
         return out, bufs, True
     out, bufs = dense_attention(q, k, v, desc, bufs=bufs, out=out, stream=stream)

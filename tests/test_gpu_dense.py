@@ -130,6 +130,32 @@ def test_schedule_routes_dense_steps_and_layers():
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), (step, layer)
 
 
+def test_schedule_quant_skips_run_floating_point_sparse():
+    """fp8 configuration with quantised-path skips: the named sparse forwards equal
+    bf16 sparse attention, the others fp8 sparse attention, dense steps the fp8
+    dense path (bit for bit)."""
+    import dataclasses
+    import torch
+    import block_sparse_video_rf_amd as rf
+    w = WORKLOADS["tiny"].with_(precision="fp8")
+    desc = rf.Desc.from_workload(w)
+    q, k, v = (to_dev(x) for x in make_qkv(w))
+    sched = rf.DenseSchedule(start_step=1)
+    skips = rf.QuantSkips(skip_steps="2", skip_layers="4")
+    fp8_sparse, _ = rf.attention(q, k, v, desc)
+    fp8_dense, _ = rf.dense_attention(q, k, v, desc)
+    bf16_sparse, _ = rf.attention(q, k, v, dataclasses.replace(desc, precision="bf16"))
+    bufs = None
+    for step, layer, ref, want_sparse in ((0, 0, fp8_dense, False), (1, 0, fp8_sparse, True),
+                                          (2, 0, bf16_sparse, True), (1, 4, bf16_sparse, True),
+                                          (3, 1, fp8_sparse, True), (0, 4, fp8_dense, False)):
+        out, bufs, used_sparse = rf.scheduled_attention(q, k, v, desc, sched, step, 4, layer,
+                                                        bufs=bufs, quant_skips=skips)
+        torch.cuda.synchronize()
+        assert used_sparse == want_sparse
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), (step, layer)
+
+
 def test_schedule_routes_geometry_fallback_dense():
     """31 sparse blocks (below the 32-block threshold): dense on every step."""
     import torch

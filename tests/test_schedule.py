@@ -3,7 +3,7 @@ Configuration: start_step early steps and end_step final steps stay dense, so
 do the DiT blocks that skip_layers names. Pure host logic."""
 import pytest
 
-from block_sparse_video_rf_amd import DenseSchedule, parse_layers
+from block_sparse_video_rf_amd import DenseSchedule, QuantSkips, parse_layers, route
 
 
 def test_selector_of_the_configuration_table():
@@ -65,3 +65,36 @@ def test_out_of_range_queries_raise():
         s.sparse(-1, 10, 0)
     with pytest.raises(ValueError):
         s.sparse(0, 10, -1)
+
+
+def test_quant_skips_route_named_sparse_forwards_to_bf16():
+    # "Wan2.2 T2V quantization": for 40 steps the page recommends skip_steps
+    # "0,1,38,39" and skip_layers "0,39"; those forwards stay sparse in floating point.
+    skips = QuantSkips(skip_steps="0,1,38,39", skip_layers="0,39")
+    sched = DenseSchedule()
+    for step in range(40):
+        for layer in range(40):
+            named = step in (0, 1, 38, 39) or layer in (0, 39)
+            assert route(sched, skips, "fp8", step, 40, layer) == (
+                "sparse", "bf16" if named else "fp8")
+            # bf16 is unaffected; so is everything without skips
+            assert route(sched, skips, "bf16", step, 40, layer) == ("sparse", "bf16")
+            assert route(sched, None, "fp8", step, 40, layer) == ("sparse", "fp8")
+
+
+def test_dense_schedule_decides_first_in_the_shared_precision():
+    # Warm-up steps and layer exclusions select dense attention in the configured
+    # precision, whatever the quantised-path skips say.
+    sched = DenseSchedule(start_step=2, end_step=1, skip_layers="5")
+    skips = QuantSkips(skip_steps=[0, 3], skip_layers=[5, 7])
+    assert route(sched, skips, "fp8", 0, 10, 1) == ("dense", "fp8")     # warm-up and skipped step
+    assert route(sched, skips, "fp8", 9, 10, 1) == ("dense", "fp8")     # final step
+    assert route(sched, skips, "mix", 4, 10, 5) == ("dense", "mix")     # excluded layer
+    assert route(sched, skips, "fp8", 3, 10, 1) == ("sparse", "bf16")   # skipped step
+    assert route(sched, skips, "fp8", 4, 10, 7) == ("sparse", "bf16")   # skipped layer
+    assert route(sched, skips, "fp8", 4, 10, 1) == ("sparse", "fp8")
+    # Fixed indices: step 39 is not "the last step" of a 50-step run.
+    s40 = QuantSkips(skip_steps="38,39")
+    assert route(DenseSchedule(), s40, "fp8", 49, 50, 3) == ("sparse", "fp8")
+    with pytest.raises(ValueError):
+        QuantSkips(skip_steps="3-1")

@@ -33,6 +33,17 @@ import oracle
 from oracle.geometry import Geometry
 from synth import bf16_to_f32
 
+# mxfp4 against the oracle's mxfp4 reading on the same codes: the kernel takes
+# logits and exponentials in fp32, the oracle in float64, so a P next to an E2M1
+# rounding midpoint (or a block maximum next to 7.25 * 2^e) can land on the
+# neighbouring code: one E2M1 step, up to half of that P. A CPU simulation of the
+# kernel's one-pass fp32 arithmetic (running integer reference, per-lane 32-key
+# MX blocks, exp2 with 1-ulp noise) against the oracle on the small cases gives
+# max 5.6e-3, mean 1.1e-4 and no element beyond 2e-2 (3.4M, 0.6M and 3.1M
+# outputs). The mean bound is the bf16 one; the max bound leaves room for one
+# flipped P in a short, peaked row (a share w of the row moves the output by up
+# to w/2 * max|v - O|), and at most 0.5% of the outputs may exceed the bf16 max
+# bound.
 MXFP4_TOL = (0.25, 2e-3)
 # The library refuses mxfp4 in its device entry points for now (RF_ERR_UNSUPPORTED):
 # the mxfp4 attention kernel faulted the GPU on its first runs (it read the fp8

@@ -139,6 +139,11 @@ rf_status rf_derive(const rf_desc* d, RfGeom* g, rf_plan_info* info) {
     info->v_scale_elems = (int64_t)r.B * r.N2 * r.n_blocks;
     info->ws_select_bytes =
         r.fallback ? 0 : rf_ws_scores_bytes(r) + rf_ws_qpool_bytes(r) + rf_ws_kpool_bytes(r);
+    // K-side buffers that the attention kernel reads in 128-row tiles end with
+    // RF_K_SLACK_ROWS rows of slack: the tile of a short last block reads past
+    // the last head's rows (masked), and the slack keeps that inside the buffer.
+    const int64_t slack = (int64_t)RF_K_SLACK_ROWS * r.D;  // elements of one head's slack
+    info->kp_bytes = 2 * (info->kp_elems + slack);
     switch (d->precision) {
       case RF_PREC_BF16:
         info->vpt_bytes = 2 * info->vpt_elems;
@@ -146,7 +151,7 @@ rf_status rf_derive(const rf_desc* d, RfGeom* g, rf_plan_info* info) {
       case RF_PREC_MIX:
       case RF_PREC_FP8:
         info->q8_bytes = info->qp_elems;
-        info->k8_bytes = info->kp_elems;
+        info->k8_bytes = info->kp_elems + slack;
         info->vpt_bytes = (d->precision == RF_PREC_FP8 ? 1 : 2) * info->vpt_elems;
         info->q_scale_bytes = 4 * info->q_scale_elems;
         info->k_scale_bytes = 4 * info->k_scale_elems;
@@ -154,10 +159,10 @@ rf_status rf_derive(const rf_desc* d, RfGeom* g, rf_plan_info* info) {
         break;
       default:  // RF_PREC_MXFP4
         info->q8_bytes = info->qp_elems / 2;
-        info->k8_bytes = info->kp_elems / 2;
+        info->k8_bytes = (info->kp_elems + slack) / 2;
         info->vpt_bytes = info->vpt_elems / 2;
         info->q_scale_bytes = info->qp_elems / 32;
-        info->k_scale_bytes = info->kp_elems / 32;
+        info->k_scale_bytes = (info->kp_elems + slack) / 32;
         info->v_scale_bytes = (int64_t)r.B * r.N2 * r.n_blocks * 4 * r.D;
         break;
     }
@@ -189,10 +194,10 @@ rf_status rf_permute(const rf_desc* desc, const void* q, const void* k, const vo
   if (v && !vpt) return RF_ERR_NULL;
   if (qk8 && ((q && (!q8 || !q_scale)) || (k && (!k8 || !k_scale)))) return RF_ERR_PRECISION;
   if (v8 && v && !v_scale) return RF_ERR_PRECISION;
-  const size_t qb = (size_t)pi.qp_elems * 2, kb = (size_t)pi.kp_elems * 2;
-  const size_t vb = kb;
+  const size_t qb = (size_t)pi.qp_elems * 2, kb = (size_t)pi.kp_bytes;
+  const size_t vb = (size_t)pi.kp_elems * 2;
   const void* ins[3] = {q, k, v};
-  const size_t insz[3] = {qb, kb, vb};
+  const size_t insz[3] = {qb, vb, vb};
   const void* outs[10] = {qp, kp, vpt, q_pool, k_pool, q8, k8, q_scale, k_scale, v_scale};
   const size_t outsz[10] = {qb, kb, (size_t)pi.vpt_bytes,
                             (size_t)pi.q_pool_elems * 4, (size_t)pi.k_pool_elems * 4,
@@ -246,7 +251,7 @@ static rf_status attn_operands(const rf_desc* desc, const RfGeom& g, const rf_pl
     return RF_ERR_NULL;
   }
   const size_t ob = (size_t)pi.qp_elems * 2;
-  if ((!qk8 && (overlaps(out_p, ob, qp, ob) || overlaps(out_p, ob, kp, (size_t)pi.kp_elems * 2))) ||
+  if ((!qk8 && (overlaps(out_p, ob, qp, ob) || overlaps(out_p, ob, kp, (size_t)pi.kp_bytes))) ||
       overlaps(out_p, ob, vpt, (size_t)pi.vpt_bytes) ||
       (qk8 && (overlaps(out_p, ob, q8, (size_t)pi.q8_bytes) ||
                overlaps(out_p, ob, k8, (size_t)pi.k8_bytes) ||

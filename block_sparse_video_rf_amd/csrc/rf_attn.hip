@@ -153,11 +153,14 @@ typedef const float __attribute__((address_space(4)))* scale_ptr;
 // maxima (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-// Raw buffer descriptor over [base, base + bytes): a load whose VGPR offset
-// is past the end returns zeros. Only the VGPR offset (with the instruction's
-// immediate) is range-checked, not the SGPR offset, so every load below puts
-// its whole offset in the VGPR operand. (Third dword: the raw 32-bit data
-// format used for plain byte-addressed buffers on gfx9.)
+// Raw buffer descriptor over [base, base + bytes). The hardware range-checks
+// only the VGPR offset (with the instruction's immediate), not the SGPR
+// offset: the tile loads below put the block offset in the SGPR operand (a
+// VGPR add per load costs 5% in bf16), so they are not clamped. They stay
+// inside their buffers by construction: V tiles are whole blocks, and the K
+// buffers end with 128 rows of slack for the tile of a short last block.
+// (Third dword: the raw 32-bit data format used for plain byte-addressed
+// buffers on gfx9.)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
@@ -605,9 +608,9 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
                           ((int64_t)b * g.N2 + nk) * g.n_blocks * (int64_t)VSC,
                       (uint32_t)((int64_t)g.n_blocks * VSC))
          : raw_buffer(nullptr, 0);
-  // K rows past a short block's end are the next rows of K, or zeros past the
-  // end of this (batch, kv head)'s K (and K scales): the offsets are range
-  // checked. They are masked out of the softmax.
+  // K rows past a short block's end are the next rows of K, or (after the last
+  // head's rows) the slack rows that end the K buffers; they are masked out of
+  // the softmax.
   // (Named registers rather than an array: they must never live in scratch.)
   static_assert(NSTG <= 8, "staging size");
   u32x4 st0, st1, st2, st3, st4, st5, st6, st7;
@@ -615,7 +618,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   static_assert(NSC <= 256, "scale chunks per group");
 #define RF_GLD1(VAR, M)                                                                    \
   if constexpr ((M) < NSTG) {                                                              \
-    if ((M) < nch_) VAR = __builtin_amdgcn_raw_buffer_load_b128(rs_, gt * 16 + so_ + (M) * 4096, 0, 0); \
+    if ((M) < nch_) VAR = __builtin_amdgcn_raw_buffer_load_b128(rs_, gt * 16, so_ + (M) * 4096, 0); \
   }
 #define RF_KST1(BUF, VAR, M)                                                               \
   if constexpr ((M) < K_CH) {                                                              \
@@ -632,7 +635,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
 // rows (kslot8 keeps the low two bits of the row).
 #define RF_GLDS(RS, SO)                                                                    \
   if constexpr (F4) {                                                                      \
-    if (gt < NSC) sts = __builtin_amdgcn_raw_buffer_load_b128((RS), gt * 16 + (SO), 0, 0); \
+    if (gt < NSC) sts = __builtin_amdgcn_raw_buffer_load_b128((RS), gt * 16, (SO), 0);     \
   }
 #define RF_VSST(BUF)                                                                       \
   if constexpr (F4) {                                                                      \

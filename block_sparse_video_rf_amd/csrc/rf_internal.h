@@ -124,3 +124,8 @@ inline size_t rf_ws_kpool_bytes(const RfGeom& g) {
 
 // Largest n_sparse the selection kernel holds in LDS.
 #define RF_MAX_SPARSE_BLOCKS 8192
+
+// Rows of slack after the last head's rows in kp, k8 and (mxfp4) k_scale: a
+// 128-row K tile that starts at a short last block reads up to 127 rows past
+// the end of the sequence.
+#define RF_K_SLACK_ROWS 128

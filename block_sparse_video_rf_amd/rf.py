@@ -48,7 +48,7 @@ class RfPlanInfo(ctypes.Structure):
         ("v_scale_elems", ctypes.c_int64), ("ws_select_bytes", ctypes.c_size_t),
         ("q8_bytes", ctypes.c_int64), ("k8_bytes", ctypes.c_int64), ("vpt_bytes", ctypes.c_int64),
         ("q_scale_bytes", ctypes.c_int64), ("k_scale_bytes", ctypes.c_int64),
-        ("v_scale_bytes", ctypes.c_int64),
+        ("v_scale_bytes", ctypes.c_int64), ("kp_bytes", ctypes.c_int64),
     ]
 
     def as_dict(self):
@@ -237,26 +237,34 @@ class Buffers:
         v8 = prec in (PREC_FP8, PREC_MXFP4)   # quantised V
         f4 = prec == PREC_MXFP4
         u8, f32 = torch.uint8, torch.float32
+
+        def with_slack(shape, dtype, nbytes):
+            """A [shape] view at the start of an allocation of ``nbytes`` (the K
+            buffers end with the slack rows rf_plan asks for)."""
+            esize = torch.empty((), dtype=dtype).element_size()
+            flat = torch.empty((nbytes // esize,), dtype=dtype, device=device)
+            return flat[:math.prod(shape)].view(shape)
+
         self.qp = None if mix else torch.empty((B, N1, S, D), dtype=bf, device=device)
-        self.kp = None if mix else torch.empty((B, N2, S, D), dtype=bf, device=device)
+        self.kp = None if mix else with_slack((B, N2, S, D), bf, info.kp_bytes)
         if f4:
             self.vpt = torch.empty((B, N2, nB, D, 64), dtype=u8, device=device)
             self.v_scale = torch.empty((B, N2, nB, 4, D), dtype=u8, device=device)
             self.q8 = torch.empty((B, N1, S, D // 2), dtype=u8, device=device)
-            self.k8 = torch.empty((B, N2, S, D // 2), dtype=u8, device=device)
+            self.k8 = with_slack((B, N2, S, D // 2), u8, info.k8_bytes)
             self.q_scale = torch.empty((B, N1, S, D // 32), dtype=u8, device=device)
-            self.k_scale = torch.empty((B, N2, S, D // 32), dtype=u8, device=device)
+            self.k_scale = with_slack((B, N2, S, D // 32), u8, info.k_scale_bytes)
         else:
             self.vpt = torch.empty((B, N2, nB, D, 128), dtype=u8 if v8 else bf, device=device)
             self.v_scale = torch.empty((B, N2, nB), dtype=f32, device=device) if v8 else None
             self.q8 = torch.empty((B, N1, S, D), dtype=u8, device=device) if mix else None
-            self.k8 = torch.empty((B, N2, S, D), dtype=u8, device=device) if mix else None
+            self.k8 = with_slack((B, N2, S, D), u8, info.k8_bytes) if mix else None
             self.q_scale = torch.empty((B, N1, nB), dtype=f32, device=device) if mix else None
             self.k_scale = torch.empty((B, N2, nB), dtype=f32, device=device) if mix else None
         # Every precision-dependent buffer has the size rf_plan gives for it.
-        for name in ("q8", "k8", "vpt", "q_scale", "k_scale", "v_scale"):
+        for name in ("q8", "k8", "vpt", "q_scale", "k_scale", "v_scale") + (() if mix else ("kp",)):
             t = getattr(self, name)
-            nbytes = 0 if t is None else t.numel() * t.element_size()
+            nbytes = 0 if t is None else t.untyped_storage().nbytes()
             if nbytes != getattr(info, name + "_bytes"):
                 raise AssertionError(f"{name}: {nbytes} bytes, rf_plan says {getattr(info, name + '_bytes')}")
         self.q_pool = torch.empty((B, N1, nS, D), dtype=f32, device=device) if lists else None

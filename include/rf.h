@@ -156,15 +156,20 @@ typedef struct rf_plan_info {
   int64_t v_scale_elems;    /* fp32 elements of v_scale (fp8): batch*heads_kv*n_blocks */
   size_t ws_select_bytes;   /* workspace of rf_pool_select */
   /* Bytes of the precision-dependent buffers for desc->precision (0 where the
-   * precision does not use the buffer):
+   * precision does not use the buffer). Buffers of K (kp, k8, and k_scale in
+   * mxfp4) end with the slack of 128 rows of one head (K128 = 128*head_dim
+   * elements): the attention kernel reads K in 128-row tiles, and the tile of
+   * a short last block reads past the last head's rows. rf_permute writes only
+   * the real rows; the slack's contents do not matter.
    *           bf16        mix            fp8            mxfp4
    *   q8      0           qp_elems       qp_elems       qp_elems / 2
-   *   k8      0           kp_elems       kp_elems       kp_elems / 2
+   *   k8      0           kp_elems+K128  kp_elems+K128  (kp_elems+K128) / 2
    *   vpt     2*vpt_elems 2*vpt_elems    vpt_elems      vpt_elems / 2
-   *   q_scale 0           4*q_scale_elems 4*q_scale_elems batch*heads_q*seq_len*head_dim/32
-   *   k_scale 0           4*k_scale_elems 4*k_scale_elems batch*heads_kv*seq_len*head_dim/32
+   *   q_scale 0           4*q_scale_elems 4*q_scale_elems qp_elems / 32
+   *   k_scale 0           4*k_scale_elems 4*k_scale_elems (kp_elems+K128) / 32
    *   v_scale 0           0              4*v_scale_elems batch*heads_kv*n_blocks*4*head_dim */
   int64_t q8_bytes, k8_bytes, vpt_bytes, q_scale_bytes, k_scale_bytes, v_scale_bytes;
+  int64_t kp_bytes;         /* bytes to allocate for kp: 2 * (kp_elems + K128) */
 } rf_plan_info;
 
 /* Validate `desc` and derive the arrangement. Host only: touches no device,
@@ -185,7 +190,7 @@ rf_status rf_plan(const rf_desc* desc, rf_plan_info* info);
  * Any of q, k, v may be NULL to skip that tensor.
  * Outputs (device), all optional unless stated:
  *   qp     bf16 [B, N1, S, D] permuted rows (BNSD whatever the input layout)
- *   kp     bf16 [B, N2, S, D]
+ *   kp     bf16 [B, N2, S, D] (allocate kp_bytes: 128 rows of slack follow)
  *   vpt    bf16 [B, N2, n_blocks, D, 128]: V block-transposed, vpt[b,n,j,d,c]
  *          = V row c of block j, channel d; columns c >= the block's length are 0.
  *          Required when v is given (it is the layout rf_sparse_attn reads).

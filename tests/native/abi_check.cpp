@@ -101,12 +101,12 @@ int main(int argc, char** argv) {
   auto* k = dev_alloc<uint16_t>(nk, owned);
   auto* v = dev_alloc<uint16_t>(nk, owned);
   auto* qp = qk8 ? nullptr : dev_alloc<uint16_t>(nq, owned);
-  auto* kp = qk8 ? nullptr : dev_alloc<uint16_t>(nk, owned);
+  auto* kp = qk8 ? nullptr : dev_alloc<uint16_t>(pi.kp_bytes / 2, owned);  // with the slack rows
   auto* vpt = dev_alloc<uint16_t>(pi.vpt_elems, owned);  // E4M3 codes need half of it
   auto* q_pool = dev_alloc<float>(pi.q_pool_elems, owned);
   auto* k_pool = dev_alloc<float>(pi.k_pool_elems, owned);
   auto* q8 = qk8 ? dev_alloc<uint8_t>(nq, owned) : nullptr;
-  auto* k8 = qk8 ? dev_alloc<uint8_t>(nk, owned) : nullptr;
+  auto* k8 = qk8 ? dev_alloc<uint8_t>(pi.k8_bytes, owned) : nullptr;
   auto* q_scale = qk8 ? dev_alloc<float>(pi.q_scale_elems, owned) : nullptr;
   auto* k_scale = qk8 ? dev_alloc<float>(pi.k_scale_elems, owned) : nullptr;
   auto* v_scale = v8 ? dev_alloc<float>(pi.v_scale_elems, owned) : nullptr;

@@ -147,8 +147,11 @@ def test_mxfp4_sizes_planned_and_device_entry_points_refused():
     d.precision = "mxfp4"
     info = rf.rf_plan(d)
     B, N1, N2, S, D = d.batch, d.heads_q, d.heads_kv, d.seq_len, d.head_dim
-    assert info.q8_bytes == B * N1 * S * D // 2 and info.k8_bytes == B * N2 * S * D // 2
-    assert info.q_scale_bytes == B * N1 * S * D // 32 and info.k_scale_bytes == B * N2 * S * D // 32
+    slack = 128 * D                                   # one head's 128 rows after the last head
+    assert info.q8_bytes == B * N1 * S * D // 2 and info.k8_bytes == (B * N2 * S * D + slack) // 2
+    assert info.q_scale_bytes == B * N1 * S * D // 32
+    assert info.k_scale_bytes == (B * N2 * S * D + slack) // 32
+    assert info.kp_bytes == 2 * (B * N2 * S * D + slack)
     assert info.vpt_bytes == B * N2 * info.n_blocks * D * 64
     assert info.v_scale_bytes == B * N2 * info.n_blocks * 4 * D
     lib = load_library()
@@ -166,6 +169,7 @@ def test_mxfp4_sizes_planned_and_device_entry_points_refused():
         d.precision = prec
         i = rf.rf_plan(d)
         assert i.q8_bytes == q8 * i.qp_elems and i.vpt_bytes == vpt * i.vpt_elems
+        assert i.k8_bytes == q8 * (i.kp_elems + slack) and i.kp_bytes == 2 * (i.kp_elems + slack)
 
 
 def test_status_strings():

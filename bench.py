@@ -33,7 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "sparse attn ms/call + dense-equiv TFLOPS & MFMA util at 0.8 sparsity, 1 MI355X"
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
 HBM_PEAK_GBS = 8000.0
 ATTN_SRC = os.path.join(ROOT, "block_sparse_video_rf_amd", "csrc", "rf_attn.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_kernel_wan22_pmc.txt")
@@ -306,6 +306,8 @@ def main():
         peak = 2.0 / (1.0 / PEAK_TFLOPS["fp8"] + 1.0 / PEAK_TFLOPS["bf16"])  # QK^T fp8, PV bf16
     elif w.precision == "fp8":
         peak = PEAK_TFLOPS["fp8"]                                            # both products fp8
+    elif w.precision == "mxfp4":
+        peak = PEAK_TFLOPS["fp4"]                                            # both products fp4
     ceiling = dense_flops / flops
 
     dense = None
@@ -344,10 +346,11 @@ def main():
 
     S, D, N1, N2, B = w.seq_len, w.head_dim, w.heads_q, w.heads_kv, w.batch
     # permute: read Q, K, V once; write the permuted Q/K (bf16, or E4M3 codes in mix
-    # and fp8), the block-transposed V (blocks padded to 128 columns; E4M3 in fp8)
-    # and the pooled means.
-    qk_out = 2 if w.precision == "bf16" else 1
-    v_out = 1 if w.precision == "fp8" else 2
+    # and fp8, E2M1 codes plus one E8M0 byte per 32 in mxfp4), the block-transposed V
+    # (blocks padded to 128 columns; E4M3 in fp8, E2M1 plus scales in mxfp4) and the
+    # pooled means.
+    qk_out = {"bf16": 2.0, "mix": 1.0, "fp8": 1.0, "mxfp4": 0.5 + 1.0 / 32}[w.precision]
+    v_out = {"bf16": 2.0, "mix": 2.0, "fp8": 1.0, "mxfp4": 0.5 + 1.0 / 32}[w.precision]
     perm_bytes = (2.0 * S * D * B * (N1 + 2 * N2) + qk_out * S * D * B * (N1 + N2)
                   + v_out * nB * 128 * D * B * N2 + 4.0 * info.n_sparse * D * B * (N1 + N2))
     unperm_bytes = 4.0 * S * D * B * N1
@@ -371,7 +374,8 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "mix": "fp8e4m3-qk/bf16-pv", "fp8": "fp8e4m3"}[w.precision],
+        "dtype": {"bf16": "bf16", "mix": "fp8e4m3-qk/bf16-pv", "fp8": "fp8e4m3",
+                  "mxfp4": "mxfp4"}[w.precision],
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads_q": N1, "heads_kv": N2, "head_dim": D,
                    "seq_len": S, "prefix_len": w.prefix_len, "grid": list(w.grid),

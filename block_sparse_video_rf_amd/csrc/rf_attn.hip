@@ -656,7 +656,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
   }
 // Tile J into the staging registers: K rows (as 16-byte chunks, row-major)
 // or V^T. Chunk m of thread gt is bytes [16 (256 m + gt), +16) of the tile in
-// both cases; rows past the end of K read as zeros (and are masked anyway).
+// both cases; rows past the end of K read the K buffer's slack rows (masked).
 #define RF_LOAD_TILE(RS, SO, NCH)                                                          \
   do {                                                                                     \
     const __amdgpu_buffer_rsrc_t rs_ = (RS);                                               \

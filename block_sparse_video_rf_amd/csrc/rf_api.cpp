@@ -21,11 +21,9 @@ namespace {
 
 bool valid_layout(int32_t l) { return l == RF_LAYOUT_BNSD || l == RF_LAYOUT_TND; }
 
-// The mxfp4 kernels are built but switched off: their first hardware runs
-// faulted (the attention kernel read the fp8 block scale through a pointer
-// that is not set in mxfp4; fixed), and they stay off until the fixed
-// kernels have passed their parity check on the hardware. rf_plan still
-// reports the precision's buffer sizes.
+// The mxfp4 kernels are built but switched off until they have passed their
+// parity check on the hardware: the device entry points refuse the precision
+// with RF_ERR_UNSUPPORTED, and rf_plan still reports its buffer sizes.
 constexpr bool kMxfp4Enabled = false;
 bool mxfp4_off(const rf_desc* d) { return d->precision == RF_PREC_MXFP4 && !kMxfp4Enabled; }
 

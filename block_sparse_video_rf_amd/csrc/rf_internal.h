@@ -47,6 +47,22 @@ RF_HD void rf_block_rows(const RfGeom& g, int32_t j, int64_t* row0, int32_t* len
   *len = (int32_t)(n < 128 ? n : 128);
 }
 
+// MXFP4 block exponent ("MXAttention: Data-Free Optimal Scaling and
+// Pre-Normalization Quantization for MXFP4 Attention", abstract: power-of-two
+// scales with the boundary Qmax = 7.25): the smallest e with
+// amax <= 7.25 * 2^e, clamped to the E8M0 range [-127, 127]. With
+// amax = m * 2^E, m in [1, 2), and 7.25 = 1.8125 * 2^2: e = E - 2 if
+// m <= 1.8125, else E - 1 -- exact, from the bits. Zero and subnormal maxima
+// (below 2^-126 < 7.25 * 2^-127) give -127. amax is finite and >= 0.
+RF_HD int rf_mx_scale_exp(float amax) {
+  uint32_t u;
+  __builtin_memcpy(&u, &amax, sizeof(u));
+  const int eb = (int)(u >> 23);
+  if (eb == 0) return -127;
+  const int e = eb - 129 + ((u & 0x7fffffu) > 0x680000u ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
 // Natural row of the token at permuted row r (0 <= r < S).
 RF_HD int64_t rf_natural_row(const RfGeom& g, int64_t r) {
   if (r < g.HF) return r;  // prefix and first frame keep their order

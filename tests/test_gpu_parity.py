@@ -18,7 +18,8 @@ from synth import WORKLOADS, Workload, make_qkv, to_tnd, from_tnd
 
 from gpu_harness import (BF16_TOL, FP8_E2E_TOL, FP8_TOL, MIX_TOL, MXFP4_TOL, assert_close,
                          assert_close_mx, check_selection, expected_vpt, f32, geometry_of, log,
-                         mx_param, mx_v_scale_natural, run_gpu, to_host_u16, unpack_e2m1)
+                         mx_param, mx_v_scale_natural, run_gpu, to_host_u16, unpack_e2m1,
+                         case_desc, case_inputs, full_check)
 
 pytestmark = pytest.mark.gpu
 
@@ -64,113 +65,15 @@ SMALL = {
 
 
 def _inputs(w, layout):
-    if w.grid == (0, 0, 0):
-        rng_w = w.with_(grid=(1, 1, 1), prefix_len=w.prefix_len - 1)
-        q, k, v = make_qkv(rng_w)
-    else:
-        q, k, v = make_qkv(w)
-    if layout == "TND":
-        q, k, v = to_tnd(q), to_tnd(k), to_tnd(v)
-    return q, k, v
+    return case_inputs(w, layout)
 
 
 def _desc(w, extra):
-    import block_sparse_video_rf_amd as rf
-    kw = dict(extra)
-    layout = kw.pop("layout", "BNSD")
-    if w.grid == (0, 0, 0):
-        return rf.Desc(batch=w.batch, heads_q=w.heads_q, heads_kv=w.heads_kv,
-                       head_dim=w.head_dim, seq_len=w.prefix_len, sparsity=w.sparsity,
-                       precision=w.precision, layout=layout)
-    return rf.Desc.from_workload(w, layout=layout, **kw)
+    return case_desc(w, extra)
 
 
 def _full_check(name):
-    w, extra = SMALL[name]
-    desc = _desc(w, extra)
-    layout = desc.layout
-    log(f"[case {name}] B={w.batch} N={w.heads_q}/{w.heads_kv} D={w.head_dim} S={desc.seq_len} "
-        f"grid={desc.grid} s={w.sparsity} {w.precision} {layout}")
-    q, k, v = _inputs(w, layout)
-    res = run_gpu(desc, q, k, v)
-    bufs = res["bufs"]
-    g = geometry_of(desc)
-    p = plan(g)
-    pi = permutation(g)
-    info = bufs.info
-    assert (info.n_blocks, info.n_sparse, info.topk) == (p.n_blocks, p.n_sparse, p.topk)
-    qb, kb, vb = (from_tnd(x, w.batch) if layout == "TND" else x for x in (q, k, v))
-
-    # Step 1: permuted copies and the block-transposed V, bit for bit.
-    if bufs.qp is not None:
-        assert np.array_equal(to_host_u16(bufs.qp), oracle.permute_rows(qb, pi))
-        assert np.array_equal(to_host_u16(bufs.kp), oracle.permute_rows(kb, pi))
-    ores = oracle.run(f32(q), f32(k), f32(v), g, precision=w.precision, layout=layout,
-                      batch=w.batch)
-    if w.precision == "fp8":
-        vpt = bufs.vpt.cpu().numpy()
-        assert np.array_equal(vpt, expected_vpt(ores["v8"], p, w.head_dim))
-        assert np.array_equal(bufs.v_scale.cpu().numpy(), ores["v_scale"])
-    elif w.precision == "mxfp4":
-        vpt = unpack_e2m1(bufs.vpt.cpu().numpy())
-        assert np.array_equal(vpt, expected_vpt(ores["v4"], p, w.head_dim))
-        assert np.array_equal(mx_v_scale_natural(bufs.v_scale.cpu().numpy()),
-                              (ores["v_exp"] + 127).astype(np.uint8))
-    else:
-        vpt = to_host_u16(bufs.vpt)
-        assert np.array_equal(vpt, expected_vpt(oracle.permute_rows(vb, pi), p, w.head_dim))
-    # Step 2: pooled means.
-    if not p.fallback:
-        qpool = bufs.q_pool.cpu().numpy()
-        kpool = bufs.k_pool.cpu().numpy()
-        assert np.abs(qpool - ores["q_pool"]).max() <= 2e-6
-        assert np.abs(kpool - ores["k_pool"]).max() <= 2e-6
-    # Quantised Q/K: codes and scales, bit for bit.
-    if w.precision == "mxfp4":
-        assert np.array_equal(unpack_e2m1(bufs.q8.cpu().numpy()), ores["q4"])
-        assert np.array_equal(unpack_e2m1(bufs.k8.cpu().numpy()), ores["k4"])
-        assert np.array_equal(bufs.q_scale.cpu().numpy(), (ores["q_exp"] + 127).astype(np.uint8))
-        assert np.array_equal(bufs.k_scale.cpu().numpy(), (ores["k_exp"] + 127).astype(np.uint8))
-    elif w.precision in ("mix", "fp8"):
-        assert np.array_equal(bufs.q8.cpu().numpy(), ores["q8"])
-        assert np.array_equal(bufs.k8.cpu().numpy(), ores["k8"])
-        assert np.array_equal(bufs.q_scale.cpu().numpy(), ores["q_scale"])
-        assert np.array_equal(bufs.k_scale.cpu().numpy(), ores["k_scale"])
-    # Step 3: selection.
-    gi = bufs.select_idx.cpu().numpy()
-    gn = bufs.select_num.cpu().numpy()
-    swaps = check_selection(p, w.batch, w.heads_q, gi, gn, ores["scores"])
-    log(f"  selection: {swaps} near-tie rows")
-    # Step 4 + 5: attention with the GPU's own lists, through the inverse arrangement.
-    out = f32(to_host_u16(res["out"]))
-    ref_same_sel = oracle.run(f32(q), f32(k), f32(v), g, precision=w.precision, layout=layout,
-                              batch=w.batch, select=(gi, gn))["out"]
-    bf16_ref = ores["out"] if w.precision == "bf16" else oracle.run(
-        f32(q), f32(k), f32(v), g, layout=layout, batch=w.batch)["out"]
-    if w.precision == "mxfp4":
-        assert_close_mx(out, ref_same_sel, MXFP4_TOL, "attention (GPU lists)")
-        # End to end: MXFP4 is coarse, so the bar is the oracle's own mxfp4
-        # deviation from the unquantised result on the same inputs.
-        own = np.abs(ores["out"] - bf16_ref)
-        dev = np.abs(out.astype(np.float64) - bf16_ref)
-        log(f"  end to end vs bf16 oracle: mean-abs {dev.mean():.3e} (oracle mxfp4 {own.mean():.3e}), "
-            f"max-abs {dev.max():.3e} (oracle {own.max():.3e})")
-        assert dev.mean() <= 1.05 * own.mean() + 1e-4
-        assert dev.max() <= own.max() + MXFP4_TOL[0]
-    else:
-        assert_close(out, ref_same_sel, FP8_TOL if w.precision == "fp8" else BF16_TOL,
-                     "attention (GPU lists)")
-        tol = {"bf16": BF16_TOL, "mix": MIX_TOL, "fp8": FP8_E2E_TOL}[w.precision]
-        assert_close(out, bf16_ref, tol, "end to end vs bf16 oracle")
-    # Roundtrip: the inverse arrangement of the permuted Q is Q itself.
-    if bufs.qp is not None:
-        import torch
-        import block_sparse_video_rf_amd as rf
-        back = torch.empty_like(res["q"])
-        rf.rf_unpermute(desc, bufs.qp, back)
-        torch.cuda.synchronize()
-        assert np.array_equal(to_host_u16(back), q)
-    return res, ores
+    return full_check(*SMALL[name], name=name)
 
 
 @pytest.mark.parametrize("name", [mx_param(n) for n in sorted(SMALL)])

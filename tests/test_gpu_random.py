@@ -40,3 +40,73 @@ def test_random_geometry(seed):
     w, extra = _case(seed)
     log(f"[random {seed}] {w}")
     full_check(w, extra)
+
+
+def _prepared(seed):
+    """A case's inputs run through the path once (fills the permuted buffers)."""
+    import block_sparse_video_rf_amd as rf
+    from gpu_harness import case_desc, case_inputs, to_dev
+    w, extra = _case(seed)
+    desc = case_desc(w, extra)
+    q, k, v = case_inputs(w, extra["layout"])
+    out, b = rf.attention(to_dev(q), to_dev(k), to_dev(v), desc)
+    return w, desc, (q, k, v), b
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_dense_entry_equals_every_block_listed(seed):
+    import torch
+    import block_sparse_video_rf_amd as rf
+    w, desc, _, b = _prepared(seed)
+    nB = b.info.n_blocks
+    rows = w.batch * nB
+    idx = torch.arange(nB, dtype=torch.int32, device="cuda").repeat(rows, w.heads_q, 1)
+    num = torch.full((rows, w.heads_q), nB, dtype=torch.int32, device="cuda")
+    o_sparse = torch.empty_like(b.out_p)
+    o_dense = torch.empty_like(b.out_p)
+    rf.rf_sparse_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, b.v_scale, idx,
+                      num, nB, o_sparse)
+    rf.rf_dense_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, b.v_scale, o_dense)
+    torch.cuda.synchronize()
+    assert torch.equal(o_sparse.view(torch.int16), o_dense.view(torch.int16))
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_lists_with_invalid_entries(seed):
+    """Unsorted lists of random blocks mixed with -1 and out-of-range ids, and
+    counts past the list width (clamped), against the oracle on the valid ids."""
+    import torch
+    import block_sparse_video_rf_amd as rf
+    import oracle
+    from gpu_harness import (BF16_TOL, FP8_TOL, assert_close, f32, geometry_of, to_host_u16)
+    w, desc, (q, k, v), b = _prepared(seed)
+    nB = b.info.n_blocks
+    rows = w.batch * nB
+    rng = np.random.default_rng(100 + seed)
+    idx = np.full((rows, w.heads_q, nB), -1, dtype=np.int32)
+    num = np.zeros((rows, w.heads_q), dtype=np.int32)
+    valid_idx = np.full_like(idx, -1)
+    valid_num = np.zeros_like(num)
+    for r in range(rows):
+        for n in range(w.heads_q):
+            m = int(rng.integers(0, min(nB, 9) + 1))
+            lst = list(rng.choice(nB, size=m, replace=False))
+            junk = [-1, nB, nB + 7, -5][:int(rng.integers(0, 3))]
+            lst = lst + junk
+            rng.shuffle(lst)
+            lst = lst[:nB]
+            idx[r, n, :len(lst)] = lst
+            num[r, n] = min(len(lst) + int(rng.integers(0, 3)), nB)   # a count past the entries
+            good = [x for x in lst[:num[r, n]] if 0 <= x < nB]
+            valid_idx[r, n, :len(good)] = good
+            valid_num[r, n] = len(good)
+    out_p = torch.empty_like(b.out_p)
+    rf.rf_sparse_attn(desc, b.qp, b.kp, b.vpt, b.q8, b.k8, b.q_scale, b.k_scale, b.v_scale,
+                      torch.from_numpy(idx).cuda(), torch.from_numpy(num).cuda(), nB, out_p)
+    torch.cuda.synchronize()
+    from synth import from_tnd
+    qb, kb, vb = (from_tnd(x, w.batch) if desc.layout == "TND" else x for x in (q, k, v))
+    ref = oracle.run(f32(qb), f32(kb), f32(vb), geometry_of(desc), precision=w.precision,
+                     select=(valid_idx, valid_num), batch=w.batch)["out_p"]
+    assert_close(f32(to_host_u16(out_p)), ref, FP8_TOL if w.precision == "fp8" else BF16_TOL,
+                 f"random lists ({w.precision})")

@@ -169,12 +169,18 @@ def test_recomputed_pools_and_determinism():
     assert torch.equal(idx2, b.select_idx) and torch.equal(num2, b.select_num)
 
 
-@pytest.mark.parametrize("grid", [(5, 16, 1200), (3, 16, 8400), (3, 8, 65536)],
-                         ids=["nS600", "nS2100", "nS8192"])
+_SEL_COUNTS = [32, 64, 65, 511, 512, 513, 1024, 1025, 2048, 2049]
+
+
+@pytest.mark.parametrize("grid", [(5, 16, 1200), (3, 16, 8400), (3, 8, 65536)]
+                         + [(3, 8, 8 * n) for n in _SEL_COUNTS],
+                         ids=["nS600", "nS2100", "nS8192"] + [f"nS{n}" for n in _SEL_COUNTS])
 def test_selection_paths_by_sparse_count(grid):
     """Selection alone at 600 sparse blocks (16 keys per lane), at 2100 (above
     the register path: one workgroup per row) and at 8192 (the largest accepted,
-    the workgroup path's LDS full), against the oracle's rule."""
+    the workgroup path's LDS full), and on both sides of every dispatch
+    boundary (8, 16 and 32 keys per lane up to 512, 1024 and 2048 blocks; one
+    key per lane at 64), against the oracle's rule."""
     import torch
     import block_sparse_video_rf_amd as rf
     w = _custom("sel", 1, 1, 1, 64, 128, grid, True, 0.8)

@@ -69,3 +69,37 @@ def test_graph_replays_match_eager(precision):
         rf.attention(q2, k, v, desc, bufs=other_bufs)
         torch.cuda.synchronize()
     log(f"  graph ({precision}): 3 replays bit-equal to eager")
+
+
+def test_concurrent_host_threads():
+    """Two host threads drive the whole path at once, each with its own buffers
+    and stream (the library keeps no mutable global state): each result equals
+    the single-threaded one, bit for bit."""
+    import threading
+    import torch
+    rf, w, desc, q, k, v = _setup("bf16")
+    ref, _ = rf.attention(q, k, v, desc)
+    torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def work(tag):
+        try:
+            torch.cuda.set_device(0)
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = [rf.attention(q, k, v, desc)[0] for _ in range(4)]
+            s.synchronize()
+            results[tag] = outs
+        except Exception as e:  # reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not errors, errors
+    assert sorted(results) == [0, 1]
+    for outs in results.values():
+        for o in outs:
+            assert torch.equal(o.view(torch.int16), ref.view(torch.int16))

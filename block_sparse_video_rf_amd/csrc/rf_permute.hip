@@ -54,21 +54,10 @@ struct PermuteArgs {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// OCP E4M3, round to nearest even, finite inputs, saturating at +-448.
-__device__ __forceinline__ uint32_t e4m3_rne(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  const float af = __uint_as_float(a);
-  if (af >= 448.0f) return sign | 0x7eu;
-  if (af < 0.015625f) {                        // below 2^-6: fixed quantum 2^-9
-    const float m = __builtin_rintf(af * 512.0f);  // exact scaling, ties to even
-    return sign | (uint32_t)m;                 // m == 8 encodes 2^-6 (exponent field 1)
-  }
-  const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);  // keep 3 mantissa bits, ties to even
-  const uint32_t e = (r >> 23) - 127u + 7u;
-  return sign | (e << 3) | ((r >> 20) & 7u);
-}
+// E4M3 codes come from gfx950's v_cvt_pk_fp8_f32 (OCP E4M3, round to nearest
+// even). Every input here is finite with magnitude at most 448 (times one
+// rounding of the scale), where that conversion is the plain nearest-even
+// encoding, -0 giving the sign bit alone.
 
 // Streaming (non-temporal) stores of 16 and 8 bytes: outputs that this kernel
 // does not read again.
@@ -97,16 +86,17 @@ __device__ __forceinline__ int pow2_scale_exp(float amax) {
   return e < -126 ? -126 : (e > 127 ? 127 : e);
 }
 
-// Block-wide reductions over 256 threads through LDS, fixed order.
+// Block-wide maximum over the 256 threads: a wave reduction by lane shuffles,
+// then the four wave maxima through LDS (one barrier). A maximum does not
+// depend on the order it is taken in.
 __device__ __forceinline__ float block_max(float x, float* red) {
+  static_assert(kThreads == 4 * 64, "four waves of 64 lanes");
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
   const int tid = threadIdx.x;
-  red[tid] = x;
+  if ((tid & 63) == 0) red[tid >> 6] = x;
   __syncthreads();
-  for (int off = kThreads / 2; off > 0; off >>= 1) {
-    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
-    __syncthreads();
-  }
-  const float r = red[0];
+  const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
   return r;
 }
@@ -235,13 +225,13 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          uint32_t x = 0;
+          float f[4];
 #pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            const float f = __uint_as_float((uint32_t)tile[(cc * 16 + 4 * e + bb) * (D + 8) + d] << 16);
-            x |= e4m3_rne(f * inv) << (8 * bb);
-          }
-          w[e] = x;
+          for (int bb = 0; bb < 4; ++bb)
+            f[bb] = __uint_as_float((uint32_t)tile[(cc * 16 + 4 * e + bb) * (D + 8) + d] << 16) * inv;
+          int x = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+          x = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], x, true);
+          w[e] = (uint32_t)x;
         }
         store_stream(dst + d * 128 + cc * 16, w[0], w[1], w[2], w[3]);
       }
@@ -361,15 +351,11 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
       const int i = p * RPP + rsub;
       if (i < len) {
         const uint32_t w[4] = {val[p].x, val[p].y, val[p].z, val[p].w};
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          lo |= e4m3_rne(bf_lo(w[e]) * r) << (16 * e);
-          lo |= e4m3_rne(bf_hi(w[e]) * r) << (16 * e + 8);
-          hi |= e4m3_rne(bf_lo(w[e + 2]) * r) << (16 * e);
-          hi |= e4m3_rne(bf_hi(w[e + 2]) * r) << (16 * e + 8);
-        }
-        store_stream(q8 + base + (int64_t)i * D + c * 8, lo, hi);
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(bf_lo(w[0]) * r, bf_hi(w[0]) * r, 0, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(bf_lo(w[1]) * r, bf_hi(w[1]) * r, lo, true);
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(bf_lo(w[2]) * r, bf_hi(w[2]) * r, 0, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(bf_lo(w[3]) * r, bf_hi(w[3]) * r, hi, true);
+        store_stream(q8 + base + (int64_t)i * D + c * 8, (uint32_t)lo, (uint32_t)hi);
       }
     }
     float* sc = static_cast<float*>(kind == 0 ? a.q_scale : a.k_scale);

@@ -217,8 +217,9 @@ def cpu_baseline(w, q, k, v, gi, gn, lengths, target_s):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path would shard by head, see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: the path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(a multi-GPU version would shard it by head, which is not implemented)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     import block_sparse_video_rf_amd as rf

@@ -319,7 +319,7 @@ const char* rf_status_str(rf_status status) {
     case RF_ERR_SPARSITY: return "sparsity must be finite and in [0, 1]";
     case RF_ERR_GEOMETRY: return "video grid, prefix or first-frame rows inconsistent with seq_len";
     case RF_ERR_WORKSPACE: return "workspace smaller than rf_plan requires";
-    case RF_ERR_UNSUPPORTED: return "valid but not supported by this build (block shape 128x128, "
+    case RF_ERR_UNSUPPORTED: return "valid but not supported by the library (block shape 128x128, "
                                     "head_dim 64/128, <= 8192 sparse blocks; mxfp4 kernels are "
                                     "switched off)";
     case RF_ERR_PRECISION: return "unknown precision, or a buffer that precision needs is NULL";

@@ -21,6 +21,11 @@ Comparison rules:
   1/8 of that P. A P that carries a share w of its row then moves the output
   by at most w/8 * max|v - O|; the max bound allows w up to about 0.1 with
   |v| up to 4 (short rows of few keys), the mean bound is unchanged.
+* mix and fp8 against the unquantised oracle: the fixed bound above, or, where
+  the oracle's own quantised result already deviates further from the
+  unquantised one on the same inputs, that deviation plus the kernel's bound
+  against the quantised reading (the GPU can be no further from the
+  unquantised result than the reading is, plus its own error).
 """
 from __future__ import annotations
 
@@ -286,10 +291,23 @@ def full_check(w, extra, name=None):
         assert dev.mean() <= 1.05 * own.mean() + 1e-4
         assert dev.max() <= own.max() + MXFP4_TOL[0]
     else:
-        assert_close(out, ref_same_sel, FP8_TOL if w.precision == "fp8" else BF16_TOL,
-                     "attention (GPU lists)")
+        kernel_tol = FP8_TOL if w.precision == "fp8" else BF16_TOL
+        assert_close(out, ref_same_sel, kernel_tol, "attention (GPU lists)")
         tol = {"bf16": BF16_TOL, "mix": MIX_TOL, "fp8": FP8_E2E_TOL}[w.precision]
-        assert_close(out, bf16_ref, tol, "end to end vs bf16 oracle")
+        if w.precision == "bf16":
+            assert_close(out, bf16_ref, tol, "end to end vs bf16 oracle")
+        else:
+            # End to end: the fixed bound of the quantised precision, unless the
+            # oracle's own quantised result already deviates further from the
+            # unquantised one on these inputs (short rows of a few blocks can):
+            # then that deviation plus the kernel's bound against the quantised
+            # reading, which the check above holds.
+            own = np.abs(ores["out"] - bf16_ref)
+            dev = np.abs(out.astype(np.float64) - bf16_ref)
+            log(f"  end to end vs bf16 oracle max-abs {dev.max():.3e} mean-abs {dev.mean():.3e} "
+                f"(oracle {w.precision}: {own.max():.3e} / {own.mean():.3e}; tol {tol[0]:g}/{tol[1]:g})")
+            assert dev.max() <= max(tol[0], own.max() + kernel_tol[0]), ("max-abs", dev.max())
+            assert dev.mean() <= max(tol[1], own.mean() + kernel_tol[1]), ("mean-abs", dev.mean())
     # Roundtrip: the inverse arrangement of the permuted Q is Q itself.
     if bufs.qp is not None:
         import torch

@@ -35,7 +35,10 @@ def _case(seed):
     return w, {"layout": layout, "min_sparse_blocks": 1}
 
 
-@pytest.mark.parametrize("seed", range(10))
+# Seeds 0-9, and six mix cases of a wider one-off sweep (200 seeds) where the
+# oracle's own E4M3 Q/K result deviates 6.2e-2 to 9.9e-2 (max-abs) from the
+# unquantised one: the end-to-end bar then follows that deviation.
+@pytest.mark.parametrize("seed", list(range(10)) + [15, 74, 75, 88, 126, 202])
 def test_random_geometry(seed):
     w, extra = _case(seed)
     log(f"[random {seed}] {w}")

@@ -212,6 +212,35 @@ rf_status rf_permute(const rf_desc* desc, const void* q, const void* k, const vo
                            v8 ? v_scale : nullptr, stream);
 }
 
+// Checks of rf_pool_select's operands: the lists are
+// present and wide enough, the inputs the call reads are present, and no
+// output (lists, and the workspace when the caller gives one) overlaps an
+// input or another output.
+static rf_status pool_select_operands(const RfGeom& g, const rf_plan_info& pi, const void* qp,
+                                      const void* kp, const float* q_pool, const float* k_pool,
+                                      const int32_t* select_idx, const int32_t* select_num,
+                                      int32_t max_kv, const void* ws, size_t ws_bytes) {
+  if (!select_idx || !select_num) return RF_ERR_NULL;
+  if (max_kv < g.n_blocks) return RF_ERR_SHAPE;
+  const size_t ib = (size_t)pi.select_rows * g.N1 * (size_t)max_kv * 4;
+  const size_t nb = (size_t)pi.select_rows * g.N1 * 4;
+  if (overlaps(select_idx, ib, select_num, nb)) return RF_ERR_ALIAS;
+  if (g.fallback) return RF_OK;  // only the all-dense lists are written
+  if ((!q_pool && !qp) || (!k_pool && !kp)) return RF_ERR_NULL;
+  // Inputs the call reads: the pooled blocks, or the rows they are pooled from.
+  const void* ins[2] = {q_pool ? (const void*)q_pool : qp, k_pool ? (const void*)k_pool : kp};
+  const size_t insz[2] = {q_pool ? (size_t)pi.q_pool_elems * 4 : (size_t)pi.qp_elems * 2,
+                          k_pool ? (size_t)pi.k_pool_elems * 4 : (size_t)pi.kp_elems * 2};
+  const void* outs[3] = {select_idx, select_num, ws};
+  const size_t outsz[3] = {ib, nb, ws_bytes};
+  for (int i = 0; i < 2; ++i)
+    for (int o = 0; o < 3; ++o)
+      if (overlaps(ins[i], insz[i], outs[o], outsz[o])) return RF_ERR_ALIAS;
+  if (overlaps(ws, ws_bytes, select_idx, ib) || overlaps(ws, ws_bytes, select_num, nb))
+    return RF_ERR_ALIAS;
+  return RF_OK;
+}
+
 rf_status rf_pool_select(const rf_desc* desc, const void* qp, const void* kp, const float* q_pool,
                          const float* k_pool, int32_t* select_idx, int32_t* select_num,
                          int32_t max_kv, void* workspace, size_t workspace_bytes, void* stream) {
@@ -219,16 +248,14 @@ rf_status rf_pool_select(const rf_desc* desc, const void* qp, const void* kp, co
   rf_plan_info pi;
   rf_status s = rf_derive(desc, &g, &pi);
   if (s != RF_OK) return s;
-  if (!select_idx || !select_num) return RF_ERR_NULL;
-  if (max_kv < g.n_blocks) return RF_ERR_SHAPE;
   if (!g.fallback) {
-    if ((!q_pool && !qp) || (!k_pool && !kp)) return RF_ERR_NULL;
     if (!workspace) return RF_ERR_NULL;
     if (workspace_bytes < pi.ws_select_bytes) return RF_ERR_WORKSPACE;
   }
-  const size_t ib = (size_t)pi.select_rows * g.N1 * (size_t)max_kv * 4;
-  const size_t nb = (size_t)pi.select_rows * g.N1 * 4;
-  if (overlaps(select_idx, ib, select_num, nb)) return RF_ERR_ALIAS;
+  // The part of the workspace the call writes.
+  s = pool_select_operands(g, pi, qp, kp, q_pool, k_pool, select_idx, select_num, max_kv,
+                           workspace, rf_ws_used_bytes(g, q_pool != nullptr, k_pool != nullptr));
+  if (s != RF_OK) return s;
   return rf_launch_pool_select(g, desc->scale, qp, kp, q_pool, k_pool, select_idx, select_num,
                                max_kv, workspace, stream);
 }

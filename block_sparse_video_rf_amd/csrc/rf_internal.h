@@ -137,6 +137,16 @@ inline size_t rf_ws_qpool_bytes(const RfGeom& g) {
 inline size_t rf_ws_kpool_bytes(const RfGeom& g) {
   return rf_align256((size_t)g.B * g.N2 * g.n_sparse * g.D * 4);
 }
+// Bytes of that workspace a call actually uses: the scores, and the pool
+// pieces (in layout order) up to the last one it recomputes.
+inline size_t rf_ws_used_bytes(const RfGeom& g, bool have_q_pool, bool have_k_pool) {
+  if (g.fallback) return 0;
+  size_t n = rf_ws_scores_bytes(g);
+  if (!have_q_pool || !have_k_pool) n += rf_ws_qpool_bytes(g);
+  if (!have_k_pool) n += rf_ws_kpool_bytes(g);
+  return n;
+}
+
 
 // Largest n_sparse the selection kernel holds in LDS.
 #define RF_MAX_SPARSE_BLOCKS 8192

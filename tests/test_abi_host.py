@@ -235,3 +235,33 @@ def test_argument_errors_before_launch():
     # Nothing to do is not an error: all inputs NULL.
     assert lib.rf_permute(ctypes.byref(c), None, None, None, None, None, None, None, None, None,
                           None, None, None, None, None) == 0
+
+
+def test_pool_select_overlap_checks():
+    """rf_pool_select refuses lists or a workspace that
+    overlap what the call reads (the pooled blocks, or the rows they are pooled
+    from), before any launch."""
+    lib = load_library()
+    d = _good()
+    c = d.c()
+    info = rf.rf_plan(d)
+    P = ctypes.c_void_p
+    big = 1 << 40
+    qp, kp, qpool, kpool, idx, num, ws = (P(big * i) for i in range(1, 8))
+    nb = info.n_blocks
+    wsb = info.ws_select_bytes
+    # Workspace on top of the pooled Q blocks, of K, or of the lists.
+    assert lib.rf_pool_select(ctypes.byref(c), None, None, qpool, kpool, idx, num, nb, qpool,
+                              wsb, None) == 13
+    assert lib.rf_pool_select(ctypes.byref(c), None, kp, qpool, None, idx, num, nb, kp, wsb,
+                              None) == 13
+    assert lib.rf_pool_select(ctypes.byref(c), None, None, qpool, kpool, idx, num, nb, idx, wsb,
+                              None) == 13
+    # selectIdx over the pooled K blocks; selectNum inside selectIdx.
+    assert lib.rf_pool_select(ctypes.byref(c), None, None, qpool, kpool, kpool, num, nb, ws,
+                              wsb, None) == 13
+    assert lib.rf_pool_select(ctypes.byref(c), None, None, qpool, kpool, idx, P(5 * big + 64), nb,
+                              ws, wsb, None) == 13
+    # qp is not read when the pooled Q blocks are given: no overlap to report.
+    assert lib.rf_pool_select(ctypes.byref(c), idx, None, qpool, kpool, idx, num, nb, ws, wsb,
+                              None) != 13

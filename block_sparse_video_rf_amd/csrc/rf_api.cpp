@@ -212,7 +212,7 @@ rf_status rf_permute(const rf_desc* desc, const void* q, const void* k, const vo
                            v8 ? v_scale : nullptr, stream);
 }
 
-// Checks of rf_pool_select's operands: the lists are
+// Checks shared by rf_pool_select and rf_pool_select_noalloc: the lists are
 // present and wide enough, the inputs the call reads are present, and no
 // output (lists, and the workspace when the caller gives one) overlaps an
 // input or another output.
@@ -258,6 +258,27 @@ rf_status rf_pool_select(const rf_desc* desc, const void* qp, const void* kp, co
   if (s != RF_OK) return s;
   return rf_launch_pool_select(g, desc->scale, qp, kp, q_pool, k_pool, select_idx, select_num,
                                max_kv, workspace, stream);
+}
+
+rf_status rf_pool_select_noalloc(const rf_desc* desc, const void* qp, const void* kp,
+                                 const float* q_pool, const float* k_pool, int32_t* select_idx,
+                                 int32_t* select_num, int32_t max_kv, void* stream) {
+  RfGeom g;
+  rf_plan_info pi;
+  rf_status s = rf_derive(desc, &g, &pi);
+  if (s != RF_OK) return s;
+  s = pool_select_operands(g, pi, qp, kp, q_pool, k_pool, select_idx, select_num, max_kv,
+                           nullptr, 0);
+  if (s != RF_OK) return s;
+  if (rf_ws_used_bytes(g, q_pool != nullptr, k_pool != nullptr) > RF_NOALLOC_SCRATCH_BYTES)
+    return RF_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (!g.fallback) {
+    s = rf_noalloc_scratch(&ws);
+    if (s != RF_OK) return s;
+  }
+  return rf_launch_pool_select(g, desc->scale, qp, kp, q_pool, k_pool, select_idx, select_num,
+                               max_kv, ws, stream);
 }
 
 // Operand checks shared by the two attention entry points: the buffers the
@@ -352,6 +373,8 @@ const char* rf_status_str(rf_status status) {
     case RF_ERR_PRECISION: return "unknown precision, or a buffer that precision needs is NULL";
     case RF_ERR_HIP: return "HIP launch failed";
     case RF_ERR_ALIAS: return "an output buffer overlaps an input buffer";
+    case RF_ERR_SCRATCH: return "the call needs more scratch than rf_pool_select_noalloc's fixed "
+                                "device array holds (RF_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

@@ -118,6 +118,9 @@ rf_status rf_launch_unpermute(const RfGeom& g, const void* out_p, void* out, voi
 rf_status rf_launch_pool_select(const RfGeom& g, float scale, const void* qp, const void* kp,
                                 const float* q_pool, const float* k_pool, int32_t* select_idx,
                                 int32_t* select_num, int32_t max_kv, void* ws, void* stream);
+// Device address of rf_pool_select_noalloc's fixed array on the current
+// device (looked up once per device; rf_select.hip).
+rf_status rf_noalloc_scratch(void** ptr);
 rf_status rf_launch_sparse_attn(const RfGeom& g, int32_t precision, float scale, const void* qp,
                                 const void* kp, const void* vpt, const uint8_t* q8,
                                 const uint8_t* k8, const void* q_scale, const void* k_scale,

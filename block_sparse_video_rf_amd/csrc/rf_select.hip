@@ -27,6 +27,8 @@
 //   scores, and both kernels give the same lists.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "rf_internal.h"
 
 namespace {
@@ -364,6 +366,32 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
 }
 
 }  // namespace
+
+// Workspace of rf_pool_select_noalloc: a fixed array that every device the
+// library runs on holds until the process ends (scores, then recomputed
+// pools, as in a caller's workspace). In host code `scratch` names a host-side
+// stand-in, never the device memory: host code only uses the address that
+// hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) uint8_t scratch[RF_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device id
+}  // namespace
+
+rf_status rf_noalloc_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RF_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return RF_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return RF_OK;
+}
 
 rf_status rf_launch_pool_select(const RfGeom& g, float scale, const void* qp, const void* kp,
                                 const float* q_pool, const float* k_pool, int32_t* select_idx,

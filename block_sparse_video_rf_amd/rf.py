@@ -55,8 +55,11 @@ class RfPlanInfo(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
-EXPORTS = ("rf_plan", "rf_permute", "rf_pool_select", "rf_sparse_attn", "rf_dense_attn",
-           "rf_unpermute", "rf_status_str", "rf_version")
+EXPORTS = ("rf_plan", "rf_permute", "rf_pool_select", "rf_pool_select_noalloc",
+           "rf_sparse_attn", "rf_dense_attn", "rf_unpermute", "rf_status_str", "rf_version")
+
+# Size of the fixed device array behind rf_pool_select_noalloc (RF_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 72 << 20
 
 _lib = None
 
@@ -75,11 +78,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rf_plan.argtypes = [D, ctypes.POINTER(RfPlanInfo)]
     lib.rf_permute.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.rf_pool_select.argtypes = [D, P, P, P, P, P, P, ctypes.c_int32, P, ctypes.c_size_t, P]
+    lib.rf_pool_select_noalloc.argtypes = [D, P, P, P, P, P, P, ctypes.c_int32, P]
     lib.rf_sparse_attn.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_int32, P, P]
     lib.rf_dense_attn.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
     lib.rf_unpermute.argtypes = [D, P, P, P]
-    for f in ("rf_plan", "rf_permute", "rf_pool_select", "rf_sparse_attn", "rf_dense_attn",
-              "rf_unpermute"):
+    for f in ("rf_plan", "rf_permute", "rf_pool_select", "rf_pool_select_noalloc",
+              "rf_sparse_attn", "rf_dense_attn", "rf_unpermute"):
         getattr(lib, f).restype = ctypes.c_int
     lib.rf_status_str.argtypes = [ctypes.c_int]
     lib.rf_status_str.restype = ctypes.c_char_p
@@ -188,6 +192,16 @@ def rf_pool_select(desc: Desc, qp, kp, q_pool, k_pool, select_idx, select_num, m
     _check("rf_pool_select", load_library().rf_pool_select(
         ctypes.byref(d), _ptr(qp), _ptr(kp), _ptr(q_pool), _ptr(k_pool), _ptr(select_idx),
         _ptr(select_num), int(max_kv), _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def rf_pool_select_noalloc(desc: Desc, qp, kp, q_pool, k_pool, select_idx, select_num,
+                           max_kv: int, stream=None):
+    """``rf_pool_select`` with the library's fixed device array as its workspace
+    (no allocation anywhere; calls on one device share the array)."""
+    d = desc.c()
+    _check("rf_pool_select_noalloc", load_library().rf_pool_select_noalloc(
+        ctypes.byref(d), _ptr(qp), _ptr(kp), _ptr(q_pool), _ptr(k_pool), _ptr(select_idx),
+        _ptr(select_num), int(max_kv), _stream(stream)))
 
 
 def rf_sparse_attn(desc: Desc, qp, kp, vpt, q8, k8, q_scale, k_scale, v_scale, select_idx,

@@ -31,7 +31,9 @@
  * Conventions for every entry point:
  *   - The caller owns all memory. Device pointers point to HIP device memory
  *     of the current device; the library never allocates, frees or
- *     synchronises, and keeps no mutable global state (calls are thread-safe).
+ *     synchronises. Its only mutable global state is the per-device address of
+ *     rf_pool_select_noalloc's fixed array, set once under a lock (calls are
+ *     thread-safe; see that entry point for what its shared array means).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is only enqueued on it.
  *   - Every argument is validated on the host before anything is enqueued;
@@ -68,8 +70,15 @@ typedef enum rf_status {
   RF_ERR_UNSUPPORTED = 10, /* valid per the pages but not built here (see the field docs) */
   RF_ERR_PRECISION = 11,   /* unknown precision, or a buffer its precision needs is NULL */
   RF_ERR_HIP = 12,         /* a HIP launch failed */
-  RF_ERR_ALIAS = 13        /* an output aliases an input */
+  RF_ERR_ALIAS = 13,       /* an output aliases an input */
+  RF_ERR_SCRATCH = 14      /* the call needs more scratch than rf_pool_select_noalloc's fixed
+                              device array holds (RF_NOALLOC_SCRATCH_BYTES) */
 } rf_status;
+
+/* Size of the fixed device array that rf_pool_select_noalloc uses as its
+ * workspace (72 MiB: the block scores of 8 heads x 1440 x 1440 sparse blocks
+ * plus recomputed pools fit). */
+#define RF_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
 
 typedef enum rf_layout {
   RF_LAYOUT_BNSD = 0, /* [B, N, S, D], rows of D contiguous */
@@ -243,6 +252,27 @@ rf_status rf_pool_select(const rf_desc* desc, const void* qp, const void* kp,
                          const float* q_pool, const float* k_pool, int32_t* select_idx,
                          int32_t* select_num, int32_t max_kv, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* rf_pool_select for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, outputs and errors as rf_pool_select, without the workspace: the
+ * block scores (and pooled blocks, when q_pool or k_pool is NULL) go to a fixed
+ * device array inside the library of RF_NOALLOC_SCRATCH_BYTES, one per device,
+ * which each device holds from the first call on it until the process ends.
+ * The call allocates and frees nothing (no hipMalloc, hipFree or allocating
+ * library routine); its first call on a device only looks up that device's
+ * array address (hipGetSymbolAddress, with that device current).
+ * Space needed: the scores, B*N1*n_sparse^2 floats, plus B*N1*n_sparse*D
+ * floats if q_pool is NULL, plus (B*N1 + B*N2)*n_sparse*D floats if k_pool is
+ * NULL (each piece rounded up to 256 bytes); more than the array holds returns
+ * RF_ERR_SCRATCH before anything is enqueued. Every piece is written before it
+ * is read, so nothing carries over from an earlier call.
+ * All calls on one device share its array: calls whose work can overlap on
+ * that device (other streams, other host threads) race on it; the caller must
+ * order them (for instance, one stream). */
+rf_status rf_pool_select_noalloc(const rf_desc* desc, const void* qp, const void* kp,
+                                 const float* q_pool, const float* k_pool, int32_t* select_idx,
+                                 int32_t* select_num, int32_t max_kv, void* stream);
 
 /* Step 4. [ACL] Formula: out = softmax(scale * Q K^T) V over the key rows of
  * the listed 128x128 blocks (no additive mask; short blocks contribute only

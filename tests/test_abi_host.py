@@ -173,7 +173,7 @@ def test_mxfp4_sizes_planned_and_device_entry_points_refused():
 
 
 def test_status_strings():
-    for s in range(14):
+    for s in range(15):
         assert rf.rf_status_str(s) and rf.rf_status_str(s) != "unknown status"
     assert rf.rf_status_str(99) == "unknown status"
 
@@ -238,7 +238,7 @@ def test_argument_errors_before_launch():
 
 
 def test_pool_select_overlap_checks():
-    """rf_pool_select refuses lists or a workspace that
+    """rf_pool_select and its no-allocation form refuse lists or a workspace that
     overlap what the call reads (the pooled blocks, or the rows they are pooled
     from), before any launch."""
     lib = load_library()
@@ -262,6 +262,32 @@ def test_pool_select_overlap_checks():
                               wsb, None) == 13
     assert lib.rf_pool_select(ctypes.byref(c), None, None, qpool, kpool, idx, P(5 * big + 64), nb,
                               ws, wsb, None) == 13
+    assert lib.rf_pool_select_noalloc(ctypes.byref(c), qp, kp, None, None, qp, num, nb,
+                                      None) == 13
     # qp is not read when the pooled Q blocks are given: no overlap to report.
     assert lib.rf_pool_select(ctypes.byref(c), idx, None, qpool, kpool, idx, num, nb, ws, wsb,
                               None) != 13
+
+
+def test_pool_select_noalloc_refuses_oversized_scratch():
+    """A call whose block scores do not fit the fixed device array returns
+    RF_ERR_SCRATCH before touching any device (16 heads x 1440^2 scores > 72 MiB);
+    with the pooled blocks recomputed the pieces add up (the layout of rf_plan's
+    workspace)."""
+    lib = load_library()
+    d = rf.Desc(batch=1, heads_q=16, heads_kv=2, head_dim=128, seq_len=512 + 31 * 64 * 96,
+                prefix_len=512, first_frame_rows=64 * 96, grid=(31, 64, 96), sparsity=0.9)
+    info = rf.rf_plan(d)
+    assert info.n_sparse == 1440
+    scores = 16 * 1440 * 1440 * 4
+    assert scores > rf.NOALLOC_SCRATCH_BYTES
+    P = ctypes.c_void_p
+    big = 1 << 40
+    c = d.c()
+    assert lib.rf_pool_select_noalloc(ctypes.byref(c), None, None, P(big), P(2 * big), P(3 * big),
+                                      P(4 * big), info.n_blocks, None) == 14
+    assert "scratch" in rf.rf_status_str(14)
+    # The long GQA workload fits, pools recomputed included.
+    w = WORKLOADS["gqa_long"]
+    i2 = rf.rf_plan(rf.Desc.from_workload(w))
+    assert i2.ws_select_bytes <= rf.NOALLOC_SCRATCH_BYTES

@@ -30,6 +30,7 @@ def dump_exe(tmp_path_factory):
                 'rf_status rf_launch_pool_select(const RfGeom&, float, const void*, const void*, '
                 'const float*, const float*, int32_t*, int32_t*, int32_t, void*, void*) '
                 '{ return RF_ERR_HIP; }\n'
+                'rf_status rf_noalloc_scratch(void**) { return RF_ERR_HIP; }\n'
                 'rf_status rf_launch_sparse_attn(const RfGeom&, int32_t, float, const void*, '
                 'const void*, const void*, const uint8_t*, const uint8_t*, const void*, '
                 'const void*, const void*, const int32_t*, const int32_t*, int32_t, void*, '

@@ -137,11 +137,7 @@ rf_status rf_derive(const rf_desc* d, RfGeom* g, rf_plan_info* info) {
     info->v_scale_elems = (int64_t)r.B * r.N2 * r.n_blocks;
     info->ws_select_bytes =
         r.fallback ? 0 : rf_ws_scores_bytes(r) + rf_ws_qpool_bytes(r) + rf_ws_kpool_bytes(r);
-    // K-side buffers that the attention kernel reads in 128-row tiles end with
-    // RF_K_SLACK_ROWS rows of slack: the tile of a short last block reads past
-    // the last head's rows (masked), and the slack keeps that inside the buffer.
-    const int64_t slack = (int64_t)RF_K_SLACK_ROWS * r.D;  // elements of one head's slack
-    info->kp_bytes = 2 * (info->kp_elems + slack);
+    info->kp_bytes = 2 * info->kp_elems;
     switch (d->precision) {
       case RF_PREC_BF16:
         info->vpt_bytes = 2 * info->vpt_elems;
@@ -149,7 +145,7 @@ rf_status rf_derive(const rf_desc* d, RfGeom* g, rf_plan_info* info) {
       case RF_PREC_MIX:
       case RF_PREC_FP8:
         info->q8_bytes = info->qp_elems;
-        info->k8_bytes = info->kp_elems + slack;
+        info->k8_bytes = info->kp_elems;
         info->vpt_bytes = (d->precision == RF_PREC_FP8 ? 1 : 2) * info->vpt_elems;
         info->q_scale_bytes = 4 * info->q_scale_elems;
         info->k_scale_bytes = 4 * info->k_scale_elems;
@@ -157,10 +153,10 @@ rf_status rf_derive(const rf_desc* d, RfGeom* g, rf_plan_info* info) {
         break;
       default:  // RF_PREC_MXFP4
         info->q8_bytes = info->qp_elems / 2;
-        info->k8_bytes = (info->kp_elems + slack) / 2;
+        info->k8_bytes = info->kp_elems / 2;
         info->vpt_bytes = info->vpt_elems / 2;
         info->q_scale_bytes = info->qp_elems / 32;
-        info->k_scale_bytes = (info->kp_elems + slack) / 32;
+        info->k_scale_bytes = info->kp_elems / 32;
         info->v_scale_bytes = (int64_t)r.B * r.N2 * r.n_blocks * 4 * r.D;
         break;
     }

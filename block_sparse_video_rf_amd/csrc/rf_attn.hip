@@ -155,12 +155,14 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 
 // Raw buffer descriptor over [base, base + bytes). The hardware range-checks
 // only the VGPR offset (with the instruction's immediate), not the SGPR
-// offset: the tile loads below put the block offset in the SGPR operand (a
-// VGPR add per load costs 5% in bf16), so they are not clamped. They stay
-// inside their buffers by construction: V tiles are whole blocks, and the K
-// buffers end with 128 rows of slack for the tile of a short last block.
-// (Third dword: the raw 32-bit data format used for plain byte-addressed
-// buffers on gfx9.)
+// offset, and returns zeros for a load past `bytes`. The tile loads put the
+// block offset in the SGPR operand (a VGPR add per load costs 5% in bf16),
+// which is not clamped: that is safe for every tile that ends inside its
+// (batch, kv head)'s rows (all V tiles, and every K tile but the one of a short
+// block at the end of the sequence). That one K tile is loaded with the whole
+// offset in the VGPR operand instead, so its rows past the sequence read zeros
+// and nothing outside the buffer is touched. (Third dword: the raw 32-bit data
+// format used for plain byte-addressed buffers on gfx9.)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
@@ -589,7 +591,15 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
       VQ && !F4 ? (scale_ptr)(static_cast<const float*>(a.v_scale) + ((int64_t)b * g.N2 + nk) * g.n_blocks)
                 : nullptr;
 
-  // Tile copies: buffer loads over this (batch, kv head)'s K and V^T.
+  // Tile copies: buffer loads over this (batch, kv head)'s K and V^T. Thread
+  // gt's chunk m (16 bytes) of a tile of NCH chunks per thread sits at byte
+  // 512 NCH (gt / 32) + 16 (gt % 32) + 512 m. The VGPR offset of a load is the
+  // tile's first byte plus the thread's part (one add per tile), the
+  // instruction immediate is 512 m (< 4096), and the SGPR offset is 0: the
+  // hardware checks the VGPR offset plus the immediate against the
+  // descriptor's size (the bytes of this (batch, kv head)'s K or V^T) and
+  // reads zeros past it, so the tile of a short block at the end of the
+  // sequence reads zeros past the sequence and never leaves the buffer.
   const __amdgpu_buffer_rsrc_t rk = raw_buffer(kbytes, (uint32_t)(g.S * KROW));
   const __amdgpu_buffer_rsrc_t rv = raw_buffer(vbytes, (uint32_t)((int64_t)g.n_blocks * D * VROW));
   auto k_tile_off = [&](int32_t jb) -> int {
@@ -598,6 +608,8 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     rf_block_rows(g, jb, &r0, &fl);
     return (int)(r0 * KROW);
   };
+  const int vg_k = (gt >> 5) * (512 * K_CH) + (gt & 31) * 16;
+  const int vg_v = (gt >> 5) * (512 * V_CH) + (gt & 31) * 16;
   // mxfp4 scale bytes of this (batch, kv head): K [S][D/32], V [n_blocks][4][D].
   const __amdgpu_buffer_rsrc_t rks =
       F4 ? raw_buffer(static_cast<const uint8_t*>(a.k_scale) + ((int64_t)b * g.N2 + nk) * g.S * DT,
@@ -608,26 +620,29 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
                           ((int64_t)b * g.N2 + nk) * g.n_blocks * (int64_t)VSC,
                       (uint32_t)((int64_t)g.n_blocks * VSC))
          : raw_buffer(nullptr, 0);
-  // K rows past a short block's end are the next rows of K, or (after the last
-  // head's rows) the slack rows that end the K buffers; they are masked out of
-  // the softmax.
+  // K rows past a short block's end are the next rows of K, or (past the end
+  // of the sequence) zeros; they are masked out of the softmax.
   // (Named registers rather than an array: they must never live in scratch.)
   static_assert(NSTG <= 8, "staging size");
+  static_assert(512 * 7 < 4096, "chunk offsets fit the instruction immediate");
   u32x4 st0, st1, st2, st3, st4, st5, st6, st7;
   u32x4 sts;  // mxfp4: one 16-byte chunk of the staged tile's scale bytes
   static_assert(NSC <= 256, "scale chunks per group");
 #define RF_GLD1(VAR, M)                                                                    \
   if constexpr ((M) < NSTG) {                                                              \
-    if ((M) < nch_) VAR = __builtin_amdgcn_raw_buffer_load_b128(rs_, gt * 16, so_ + (M) * 4096, 0); \
+    if ((M) < nch_) VAR = __builtin_amdgcn_raw_buffer_load_b128(rs_, vo_ + (M) * 512, 0, 0); \
   }
+// Chunk slot of thread gt's chunk M in a tile of NCH chunks per thread (the
+// byte layout above, in 16-byte units).
+#define RF_SLOT(NCH, M) ((gt >> 5) * (32 * (NCH)) + (gt & 31) + 32 * (M))
 #define RF_KST1(BUF, VAR, M)                                                               \
   if constexpr ((M) < K_CH) {                                                              \
-    const int slot_ = (M) * 256 + gt, r_ = slot_ / KCH, c_ = slot_ % KCH;                  \
+    const int slot_ = RF_SLOT(K_CH, M), r_ = slot_ / KCH, c_ = slot_ % KCH;                \
     *reinterpret_cast<u32x4*>((BUF) + (VQ ? kslot8(r_) : r_) * KSTR + c_ * 16) = VAR;      \
   }
 #define RF_VST1(BUF, VAR, M)                                                               \
   if constexpr ((M) < V_CH) {                                                              \
-    const int slot_ = (M) * 256 + gt, d_ = slot_ / VCH, c_ = slot_ % VCH;                  \
+    const int slot_ = RF_SLOT(V_CH, M), d_ = slot_ / VCH, c_ = slot_ % VCH;                \
     *reinterpret_cast<u32x4*>((BUF) + d_ * VSTR + c_ * 16) = VAR;                          \
   }
 // mxfp4 scale chunk: V^T scales copied as they are; K scales of rows
@@ -635,7 +650,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
 // rows (kslot8 keeps the low two bits of the row).
 #define RF_GLDS(RS, SO)                                                                    \
   if constexpr (F4) {                                                                      \
-    if (gt < NSC) sts = __builtin_amdgcn_raw_buffer_load_b128((RS), gt * 16, (SO), 0);     \
+    if (gt < NSC) sts = __builtin_amdgcn_raw_buffer_load_b128((RS), (SO) + gt * 16, 0, 0); \
   }
 #define RF_VSST(BUF)                                                                       \
   if constexpr (F4) {                                                                      \
@@ -654,20 +669,14 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
       }                                                                                    \
     }                                                                                      \
   }
-// Tile J into the staging registers: K rows (as 16-byte chunks, row-major)
-// or V^T. Chunk m of thread gt is bytes [16 (256 m + gt), +16) of the tile in
-// both cases; rows past the end of K read the K buffer's slack rows (masked).
-#define RF_LOAD_TILE(RS, SO, NCH)                                                          \
-  do {                                                                                     \
-    const __amdgpu_buffer_rsrc_t rs_ = (RS);                                               \
-    const int so_ = (SO), nch_ = (NCH);                                                    \
-    RF_GLD1(st0, 0) RF_GLD1(st1, 1) RF_GLD1(st2, 2) RF_GLD1(st3, 3)                        \
-    RF_GLD1(st4, 4) RF_GLD1(st5, 5) RF_GLD1(st6, 6) RF_GLD1(st7, 7)                        \
-  } while (0)
+// K tile J (as 16-byte chunks of its row-major bytes) into the staging registers.
 #define RF_LOAD_K(J)                                                                       \
   do {                                                                                     \
-    RF_LOAD_TILE(rk, k_tile_off(J), K_CH);                                                 \
-    RF_GLDS(rks, k_tile_off(J) / KROW * DT)                                                \
+    const int so_ = k_tile_off(J), nch_ = K_CH, vo_ = vg_k + so_;                          \
+    const __amdgpu_buffer_rsrc_t rs_ = rk;                                                 \
+    RF_GLD1(st0, 0) RF_GLD1(st1, 1) RF_GLD1(st2, 2) RF_GLD1(st3, 3)                        \
+    RF_GLD1(st4, 4) RF_GLD1(st5, 5) RF_GLD1(st6, 6) RF_GLD1(st7, 7)                        \
+    RF_GLDS(rks, so_ / KROW * DT)                                                          \
   } while (0)
 #define RF_STORE_K(BUF)                                                                    \
   do {                                                                                     \
@@ -767,9 +776,10 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     // The next tile's global loads ride along with the products, one after
     // every NMFMA / 8 of them, so that no wave stalls on a burst of loads.
     {
-      const __amdgpu_buffer_rsrc_t rs_ = kh == 0 ? rv : rk;
       const int so_ = kh == 0 ? jcopy * (D * VROW) : k_tile_off(jcopy);
+      const __amdgpu_buffer_rsrc_t rs_ = kh == 0 ? rv : rk;
       const int nch_ = kh == 0 ? V_CH : K_CH;
+      const int vo_ = (kh == 0 ? vg_v : vg_k) + so_;
 #define RF_Q(K) ((K) * PL::NMFMA / 8)
       if constexpr (PREC == RF_PREC_MIX) {
         // mix: all loads first (1% faster there; 2.5% slower in bf16 and fp8).
@@ -999,7 +1009,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
 #undef RF_STORE_K
 #undef RF_STORE_V
 #undef RF_GLD1
-#undef RF_LOAD_TILE
+#undef RF_SLOT
 #undef RF_KST1
 #undef RF_VST1
 #undef RF_GLDS

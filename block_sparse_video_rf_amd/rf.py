@@ -252,27 +252,20 @@ class Buffers:
         f4 = prec == PREC_MXFP4
         u8, f32 = torch.uint8, torch.float32
 
-        def with_slack(shape, dtype, nbytes):
-            """A [shape] view at the start of an allocation of ``nbytes`` (the K
-            buffers end with the slack rows rf_plan asks for)."""
-            esize = torch.empty((), dtype=dtype).element_size()
-            flat = torch.empty((nbytes // esize,), dtype=dtype, device=device)
-            return flat[:math.prod(shape)].view(shape)
-
         self.qp = None if mix else torch.empty((B, N1, S, D), dtype=bf, device=device)
-        self.kp = None if mix else with_slack((B, N2, S, D), bf, info.kp_bytes)
+        self.kp = None if mix else torch.empty((B, N2, S, D), dtype=bf, device=device)
         if f4:
             self.vpt = torch.empty((B, N2, nB, D, 64), dtype=u8, device=device)
             self.v_scale = torch.empty((B, N2, nB, 4, D), dtype=u8, device=device)
             self.q8 = torch.empty((B, N1, S, D // 2), dtype=u8, device=device)
-            self.k8 = with_slack((B, N2, S, D // 2), u8, info.k8_bytes)
+            self.k8 = torch.empty((B, N2, S, D // 2), dtype=u8, device=device)
             self.q_scale = torch.empty((B, N1, S, D // 32), dtype=u8, device=device)
-            self.k_scale = with_slack((B, N2, S, D // 32), u8, info.k_scale_bytes)
+            self.k_scale = torch.empty((B, N2, S, D // 32), dtype=u8, device=device)
         else:
             self.vpt = torch.empty((B, N2, nB, D, 128), dtype=u8 if v8 else bf, device=device)
             self.v_scale = torch.empty((B, N2, nB), dtype=f32, device=device) if v8 else None
             self.q8 = torch.empty((B, N1, S, D), dtype=u8, device=device) if mix else None
-            self.k8 = with_slack((B, N2, S, D), u8, info.k8_bytes) if mix else None
+            self.k8 = torch.empty((B, N2, S, D), dtype=u8, device=device) if mix else None
             self.q_scale = torch.empty((B, N1, nB), dtype=f32, device=device) if mix else None
             self.k_scale = torch.empty((B, N2, nB), dtype=f32, device=device) if mix else None
         # Every precision-dependent buffer has the size rf_plan gives for it.

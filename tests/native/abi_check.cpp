@@ -101,7 +101,7 @@ int main(int argc, char** argv) {
   auto* k = dev_alloc<uint16_t>(nk, owned);
   auto* v = dev_alloc<uint16_t>(nk, owned);
   auto* qp = qk8 ? nullptr : dev_alloc<uint16_t>(nq, owned);
-  auto* kp = qk8 ? nullptr : dev_alloc<uint16_t>(pi.kp_bytes / 2, owned);  // with the slack rows
+  auto* kp = qk8 ? nullptr : dev_alloc<uint16_t>(pi.kp_elems, owned);  // natural size
   auto* vpt = dev_alloc<uint16_t>(pi.vpt_elems, owned);  // E4M3 codes need half of it
   auto* q_pool = dev_alloc<float>(pi.q_pool_elems, owned);
   auto* k_pool = dev_alloc<float>(pi.k_pool_elems, owned);

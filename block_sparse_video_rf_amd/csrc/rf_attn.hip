@@ -35,9 +35,10 @@
 // scale * q_scale * k_scale of the block pair into the exponent multiplier.
 // The fp8 precision also runs O^T on E4M3 codes: V^T codes with the block's
 // power-of-two scale as the product's E8M0 operand scale, and P quantised to
-// E4M3 against an integer reference (the ceiling of the running maximum, so
-// the largest P lies in (128, 256]); an extra product of an all-ones operand
-// with P^T gives the row sums of the rounded P. The mxfp4 precision runs both
+// E4M3 with the row's power-of-two block scale (the smallest 2^m with
+// 2^(max t) <= 448 * 2^m, raised as blocks arrive, so the largest P lies in
+// (224, 448]); an extra product of an all-ones operand with P^T gives the row
+// sums of the rounded P. The mxfp4 precision runs both
 // products on E2M1 codes with one E8M0 scale per 32 values of each operand
 // lane (the MX block of the hardware: a lane's 32 contraction values): Q and
 // K scales per 32 channels, V^T scales per 32 keys, and P quantised per lane
@@ -871,18 +872,21 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     };
     // While every key so far is masked m_run is -inf; any finite stand-in keeps
     // exp2(-inf - m) at 0 instead of NaN.
-    auto ref_neg = [&]() -> float { return (VQ && !F4 ? 8.0f : 0.0f) - fmaxf(m_run, -1e30f); };
+    auto ref_neg = [&]() -> float { return -fmaxf(m_run, -1e30f); };
 
     float lsum = 0.0f;
     if constexpr (VQ) {
-      // fp8: P = 2^(t - m_run + 8) goes to E4M3 (largest finite 448), so m_run
-      // is the integer ceiling of the running maximum, raised as soon as a
-      // block exceeds it: the largest P stays in (128, 256], and the rescale by
-      // a power of two is exact and leaves the rounding of normal P unchanged.
-      // mxfp4: P = 2^(t - m_run) in MX blocks of the lane's 32 keys, with the
-      // same integer reference (the block scale absorbs any power of two).
+      // fp8: P = E4M3(2^(t - m_run)) with m_run the exponent of the row's
+      // power-of-two block scale, the smallest integer with
+      // 2^(max t) <= 448 * 2^m_run over the keys seen so far, raised as soon
+      // as a block exceeds it: the largest P stays in (224, 448], and the
+      // rescale by a power of two is exact and leaves the rounding of normal P
+      // unchanged. mxfp4: P = 2^(t - m_run) in MX blocks of the lane's 32 keys
+      // with m_run the integer ceiling of the running maximum (each MX block's
+      // own scale absorbs any power of two).
+      constexpr float kTop = F4 ? 0.0f : 8.807354922057604f;  // log2(448)
       const float lm = lane_max();
-      const float mc = max_halves(lm) * cs;
+      const float mc = max_halves(lm) * cs - kTop;
       if (__any(mc > m_run)) {
         const float m_new = fmaxf(m_run, ceilf(mc));
         rescale(m_new, m_run == -INFINITY ? 0.0f : ldexpf(1.0f, (int)(m_run - m_new)));
@@ -905,7 +909,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
         }
         c.psc = ep + 127;
       } else {
-      // P as E4M3 codes (round to nearest even; P <= 2^8 < 448), byte 16 t + v
+      // P as E4M3 codes (round to nearest even; P <= 448), byte 16 t + v
       // of the B operand. The row sum of the rounded values (what multiplies
       // V) comes from the all-ones product in the next MFMA interval.
 #pragma unroll

@@ -96,10 +96,11 @@ typedef enum rf_precision {
                        Q/K as in mix; V per (batch, kv head, 128-row block) with a
                        power-of-two scale 2^e, e the smallest integer with
                        amax <= 448 * 2^e (clamped to [-126, 127]; 0 for a zero block),
-                       code = E4M3(x / 2^e); probabilities P = E4M3(2^(t - M + 8)) with
-                       t = scale*<q,k>/ln 2 and M = ceil(row max of t) (largest P in
-                       (128, 256]), and
-                       out = sum P v / sum P (the sum of the rounded P; [MXA]).
+                       code = E4M3(x / 2^e); probabilities: each row's unnormalised
+                       exponentials 2^t (t = scale*<q,k>/ln 2) quantised before the row
+                       sum ([MXA]) with the same power-of-two block scale rule,
+                       P = E4M3(2^(t - m)), m = ceil(row max of t - log2 448) (largest P
+                       in (224, 448]), and out = sum P v / sum P (the sum of the rounded P).
                        Softmax bookkeeping and accumulation fp32, output bf16. */
   RF_PREC_MXFP4 = 3 /* all operands OCP MXFP4: E2M1 values in blocks of 32 along each
                        product's contraction, one E8M0 power-of-two scale 2^e per block.
@@ -109,8 +110,9 @@ typedef enum rf_precision {
                        code = E2M1(x / 2^e), nearest-even, saturating at +-6. Blocks: 32
                        channels of each Q and K row; for V and P the four 32-key quarters
                        of each 128-row block (a short block's quarters hold its real rows).
-                       P = MXFP4 of 2^(t - M) with t and M as in fp8 (any integer M gives
-                       the same result), out = sum P v / sum P ([MXA]). No rotation
+                       P = MXFP4 of 2^(t - M) with t as in fp8 and M = ceil(row max of t)
+                       (any integer M gives the same result), out = sum P v / sum P
+                       ([MXA]). No rotation
                        ([RFA] mentions a default rotation policy without defining it).
                        Softmax bookkeeping and accumulation fp32, output bf16.
                        At present rf_permute, rf_sparse_attn and rf_dense_attn return

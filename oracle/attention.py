@@ -17,30 +17,32 @@ Float64 throughout: logits, the row maximum, exponentials, the row sum and
 the weighted sum of V.
 
 "fp8" precision ("RainFusion Attention", Configuration, names it without a
-definition) also quantises the probabilities. Reading, after the
-pre-normalisation idea of MXAttention (catalyzex author page, abstract: the
-unnormalised softmax exponentials are quantised before the row sum, so the
-normalisation holds by construction):
+definition) also quantises the probabilities. Reading, from the MXAttention
+abstract (catalyzex author page): the unnormalised softmax exponentials are
+quantised before the row sum (pre-normalisation quantisation), so the
+normalisation holds by construction; and quantised attention operands carry
+power-of-two scales. The row of exponentials is therefore quantised exactly
+like a V block of this precision (``fp8.py``: power-of-two scale, the
+smallest one that fits the largest magnitude under 448):
 
-* logits in log2 units ``t_c = scale * <q, k_c> / ln 2``;
-* reference ``M = ceil(max_c t_c)``, the row maximum rounded up to an integer;
-* ``P_c = e4m3(2**(t_c - M + 8))`` (nearest, ties to even): the exponentials
-  scaled by a power of two so that the largest lies in (128, 256], the top
-  binades of E4M3 (largest finite 448) - the same use of the full E4M3 range
-  as the block scales of Q, K and V;
+* logits in log2 units ``t_c = scale * <q, k_c> / ln 2``, exponentials
+  ``2**t_c`` (unnormalised; no reference subtracted);
+* block scale ``2**e`` with ``e`` the smallest integer such that
+  ``max_c 2**t_c <= 448 * 2**e``, i.e. ``e = ceil(max_c t_c - log2(448))``;
+* ``P_c = e4m3(2**(t_c - e))`` (nearest, ties to even): the largest lies in
+  (224, 448], the top of E4M3's range;
 * ``O = sum_c P_c v_c / sum_c P_c`` - the row sum is the sum of the quantised
   values that multiply V.
 
-Scaling by 2**k commutes with E4M3 rounding of normal values, so a one-pass
-kernel that holds a smaller integer reference for earlier blocks rounds them
-the same way; only values below 2**-6 (subnormal, below 2**-14 of the largest
-P) can round differently, and their weight is negligible.
+A scale that put the row maximum exactly at the top of the range would in
+general not be a power of two; the power-of-two scale is what the pages'
+microscaling uses, and it is data-free (no calibration or search).
 
 "mxfp4" precision ("RainFusion Attention", Wan2.2 T2V quantization, names it;
 MXAttention, abstract, gives the pre-normalisation step). Reading, in the same
 shape as "fp8":
 
-* ``t_c`` and ``M = ceil(max_c t_c)`` as above, ``x_c = 2**(t_c - M)`` in (0, 1];
+* ``t_c`` as above, ``M = ceil(max_c t_c)``, ``x_c = 2**(t_c - M)`` in (0, 1];
 * the row's keys fall into MX blocks of 32: the quarters of each listed
   128-row block (``mxfp4.py``); each block of ``x`` is quantised to MXFP4
   with its own UOS scale, giving ``P_c``;
@@ -56,7 +58,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .fp8 import e4m3_round
+from .fp8 import E4M3_MAX, e4m3_round
 from .geometry import Plan
 from .mxfp4 import MX_BLOCK, mx_round_groups
 
@@ -72,6 +74,13 @@ def attention_block(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -
     return (e @ np.asarray(v, dtype=np.float64)) / e.sum(axis=1, keepdims=True)
 
 
+def fp8p_scale_exponent(t: np.ndarray) -> np.ndarray:
+    """Exponent ``e`` of the power-of-two block scale of each row's
+    exponentials ``2**t`` (``t [M, L]``): the smallest integer with
+    ``2**max(t) <= 448 * 2**e``, i.e. ``ceil(max t - log2 448)`` (shape ``[M, 1]``)."""
+    return np.ceil(t.max(axis=1, keepdims=True) - np.log2(E4M3_MAX))
+
+
 def attention_block_fp8p(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
     """Attention with E4M3 probabilities quantised before the row sum (float64).
 
@@ -80,8 +89,7 @@ def attention_block_fp8p(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: flo
     if k.shape[0] == 0:
         return np.zeros((q.shape[0], v.shape[1]), dtype=np.float64)
     t = (scale / np.log(2.0)) * (q @ np.asarray(k, dtype=np.float64).T)
-    ref = np.ceil(t.max(axis=1, keepdims=True))
-    pq = e4m3_round(np.exp2(t - ref + 8.0))
+    pq = e4m3_round(np.exp2(t - fp8p_scale_exponent(t)))
     return (pq @ np.asarray(v, dtype=np.float64)) / pq.sum(axis=1, keepdims=True)
 
 

@@ -29,7 +29,8 @@ The dequantised value is ``decode(code) * sigma``.
 The "fp8" precision (same Configuration row, equally undefined there) is read
 as every attention operand in E4M3: Q and K exactly as in "mix"; V per
 (batch, kv head, 128-row block) with a power-of-two scale (below); and the
-probabilities P as E4M3 codes of the unnormalised exponentials (``attention.py``).
+probabilities P as E4M3 codes of the unnormalised exponentials, each row
+quantised with the same power-of-two block scale rule as V (``attention.py``).
 
 Power-of-two block scale (V in "fp8"): ``sigma = 2**e`` with ``e`` the
 smallest integer such that ``amax <= 448 * 2**e``, clamped to [-126, 127]

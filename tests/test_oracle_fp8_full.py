@@ -1,12 +1,14 @@
 """Pins of the oracle's "fp8" precision: power-of-two V scales and E4M3
-probabilities quantised before the row sum.
+probabilities quantised before the row sum, each row with the same
+power-of-two block scale rule as V.
 
 The scale exponent is checked against a linear search; the V quantiser by
 exact round trips of E4M3-representable blocks; the probability rounding by a
 brute-force nearest-code search over the E4M3 value table (an independent
-statement of round-to-nearest-even) inside a pure-Python attention loop, and
-by closed forms that tell apart the plausible mistakes: no rounding, the
-exact maximum instead of its integer ceiling as the reference, and
+statement of round-to-nearest-even) with the row's scale exponent found by
+linear search, inside a pure-Python attention loop, and by closed forms that
+tell apart the plausible mistakes: no rounding, a scale that is not a power
+of two (the exact row maximum as the reference), a scale one binade off, and
 normalising by the unquantised sum.
 """
 import math
@@ -104,12 +106,15 @@ def test_quantize_pow2_error_and_range():
 
 
 def _fp8p_by_loops(q, k, v, scale):
-    """Pure-Python statement of the reading, with brute-force rounding."""
+    """Pure-Python statement of the reading, with brute-force rounding: the
+    row's exponentials 2^t get the smallest power-of-two scale 2^e with
+    max 2^t <= 448 * 2^e (found by search), then E4M3 codes."""
     out = []
     for qi in q:
         t = [scale / math.log(2.0) * sum(a * b for a, b in zip(qi, kc)) for kc in k]
-        ref = math.ceil(max(t))
-        pq = [_nearest_code_value(2.0 ** (tc - ref + 8)) for tc in t]
+        top = 2.0 ** max(t)
+        e = next(e for e in range(-300, 300) if top <= 448.0 * 2.0 ** e)
+        pq = [_nearest_code_value(2.0 ** (tc - e)) for tc in t]
         den = sum(pq)
         out.append([sum(pq[c] * v[c][d] for c in range(len(k))) / den for d in range(len(v[0]))])
     return np.array(out)
@@ -133,7 +138,8 @@ def _two_keys(t0, t1, v):
 
 def test_fp8p_closed_forms():
     v = np.array([[1.0, -2.0], [5.0, 7.0]])
-    # Equal logits: every P is 256, the output is the mean.
+    # Equal logits: every P is 256 (the scale 2^-8 puts 2^0 at 256 <= 448), the
+    # output is the mean.
     np.testing.assert_allclose(
         attention_block_fp8p(np.zeros((1, 3)), np.ones((4, 3)), np.arange(8.0).reshape(4, 2), 1.0),
         [[3.0, 4.0]], atol=1e-15)
@@ -143,12 +149,21 @@ def test_fp8p_closed_forms():
     # the sum of the rounded values: 256 and 240.
     np.testing.assert_allclose(_two_keys(0.0, math.log2(0.95), v),
                                (256 * v[0] + 240 * v[1]) / 496, atol=1e-15)
-    # The reference is ceil(max) = 3, not the maximum 2.3: P = (2^7.3, 2^5) rounds
-    # to (160, 32); with the maximum as reference it would be (256, 52).
-    np.testing.assert_allclose(_two_keys(2.3, 0.0, v), (5 * v[0] + v[1]) / 6, atol=1e-15)
-    # With the largest P at 2^8, a key 9.5 below it gets 2^-1.5 = 0.354, a normal
-    # value that rounds to 11/32; with the largest P at 1 it would be subnormal
-    # and round to 2^-9.
+    # A power-of-two scale, the smallest that fits: max 2^2.3 <= 448 * 2^-6 (not
+    # 2^-7), so P = (2^8.3, 2^6) = (315.2, 64) -> (320, 64). With the exact
+    # maximum as the reference (a scale that is not a power of two) it would be
+    # (2^8, 2^5.7) -> (256, 52).
+    np.testing.assert_allclose(_two_keys(2.3, 0.0, v), (320 * v[0] + 64 * v[1]) / 384, atol=1e-15)
+    # The scale exponent is the smallest that fits: 2^0.5 * 2^8 = 362 <= 448, so
+    # e = -8 and a key 15.2 below gets 2^-6.7 = 0.0096, subnormal (below 2^-6),
+    # rounded to 5 * 2^-9; a scale one binade lower (largest P in (112, 224])
+    # would give 2^-7.7 -> 2 * 2^-9 instead. 2^8.5 = 362.04 rounds to 352 (step 32).
+    np.testing.assert_allclose(_two_keys(0.5, -14.7, v),
+                               (352 * v[0] + 5 * 2.0 ** -9 * v[1]) / (352 + 5 * 2.0 ** -9),
+                               atol=1e-15)
+    # A key 9.5 below the largest (P = 256) gets 2^-1.5 = 0.354, a normal value
+    # that rounds to 11/32; with the largest P at 1 it would be subnormal and
+    # round to 2^-9.
     np.testing.assert_allclose(_two_keys(0.0, -9.5, v),
                                (256 * v[0] + (11 / 32) * v[1]) / (256 + 11 / 32), atol=1e-15)
     # Subnormal P (below 2^-6): 2^-7 is exact, 2^-9.5 rounds to 2^-9, 2^-11 to 0.
@@ -157,13 +172,34 @@ def test_fp8p_closed_forms():
     np.testing.assert_allclose(_two_keys(0.0, -17.5, v),
                                (256 * v[0] + 2.0 ** -9 * v[1]) / (256 + 2.0 ** -9), atol=1e-15)
     np.testing.assert_allclose(_two_keys(0.0, -19.0, v), v[0], atol=0)
+    # Shifting every logit by an integer scales every P by the same power of two.
+    for shift in (-40, 7, 300):
+        np.testing.assert_allclose(_two_keys(2.3 + shift, shift, v), _two_keys(2.3, 0.0, v),
+                                   atol=1e-15)
     # No keys: zeros.
     assert np.all(attention_block_fp8p(np.ones((2, 3)), np.zeros((0, 3)), np.zeros((0, 4)), 1.0) == 0)
 
 
+def test_fp8p_scale_exponent_edges():
+    """e = ceil(max t - log2 448): the largest exponential lands in (224, 448]."""
+    from oracle.attention import fp8p_scale_exponent
+    for k in range(-20, 20):
+        # Just under 448 * 2^k fits that scale; just over it needs the next one.
+        # (log2 448 is irrational: no float lands on the edge itself.)
+        t = np.array([[math.log2(448.0) + k - 1e-9, -100.0]])
+        assert fp8p_scale_exponent(t)[0, 0] == k
+        t2 = np.array([[math.log2(448.0) + k + 1e-9, -100.0]])
+        assert fp8p_scale_exponent(t2)[0, 0] == k + 1
+    rng = np.random.default_rng(12)
+    t = rng.uniform(-50, 50, (200, 7))
+    e = fp8p_scale_exponent(t)
+    top = np.exp2(t.max(axis=1, keepdims=True) - e)
+    assert np.all((top > 224.0) & (top <= 448.0 * (1 + 1e-12)))
+
+
 def test_fp8p_within_rounding_bound_of_exact_softmax():
     # |O_q - O| = |sum (P~ - P)(v - O)| / sum P~ <= max|v - O| * sum max(2^-4 P, 2^-10) / sum P~
-    # with P = 2^(t - ceil(max t) + 8) and half an E4M3 quantum per element.
+    # with P = 2^(t - e), e = ceil(max t - log2 448), and half an E4M3 quantum per element.
     rng = np.random.default_rng(8)
     q = rng.standard_normal((16, 32))
     k = rng.standard_normal((300, 32))
@@ -172,7 +208,7 @@ def test_fp8p_within_rounding_bound_of_exact_softmax():
     exact = attention_block(q, k, v, scale)
     quant = attention_block_fp8p(q, k, v, scale)
     t = scale / math.log(2.0) * (q @ k.T)
-    pe = np.exp2(t - np.ceil(t.max(axis=1, keepdims=True)) + 8)
+    pe = np.exp2(t - np.ceil(t.max(axis=1, keepdims=True) - math.log2(448.0)))
     pq = e4m3_round(pe)
     assert np.all(np.abs(pq - pe) <= np.maximum(pe * 2.0 ** -4, 2.0 ** -10))
     spread = np.abs(v[None, :, :] - exact[:, None, :]).max(axis=1)        # [16, 8]

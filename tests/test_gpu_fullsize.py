@@ -2,11 +2,19 @@
 benchmark times (the same four entry points, BNSD, one call each).
 
 Everything the oracle can do quickly is compared in full: permuted Q/K and
-block-transposed V (bit-exact), pooled means, E4M3 codes and scales (mix,
-bit-exact), selectIdx / selectNum over every row (bit-exact up to near-ties).
-The attention output is compared on sampled (query block, head) pairs that
-the float64 oracle computes one by one - every kind of query block (head,
-sparse, tail) is sampled - through the inverse arrangement.
+block-transposed V (bit-exact), pooled means, the block scores in the
+selection workspace, E4M3 codes and scales (bit-exact), selectIdx / selectNum
+over every row (bit-exact up to near-ties). The Wan2.2 data in bf16, mix and
+fp8 precision must select the same blocks (selection uses the unquantised
+Q/K in every precision).
+
+The attention output ("aclnnRainFusionAttention", Formula, over the listed
+blocks) is compared through the inverse arrangement against the float64
+oracle, spread over worker processes (tests/oracle_pool.py):
+* minimax_h3: every (query block, head) pair, the whole output;
+* the other workloads: every head at its first block, its last block, every
+  16th sparse block, and the query blocks of the last workgroup of each
+  XCD's run in both dispatch phases (dense query blocks first, then sparse).
 """
 import numpy as np
 import pytest
@@ -15,27 +23,60 @@ import oracle
 from oracle.geometry import plan, permutation
 from synth import WORKLOADS, make_qkv
 
-from gpu_harness import (BF16_TOL, FP8_E2E_TOL, FP8_TOL, MIX_TOL, MXFP4_TOL, mx_v_scale_natural,
-                         unpack_e2m1, mx_param, assert_close, check_selection,
-                         expected_vpt, f32, geometry_of, log, run_gpu, to_host_u16)
+from gpu_harness import (BF16_TOL, MIX_TOL, MXFP4_TOL, mx_v_scale_natural, unpack_e2m1, mx_param,
+                         check_selection, expected_vpt, f32, geometry_of, log, run_gpu,
+                         to_host_u16)
+from oracle_pool import compare_pairs
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+XCDS = 8
+_LISTS = {}   # selectIdx / selectNum of the Wan2.2 data, per precision
 
 
-def _samples(p, heads, rng, n_sparse=24):
-    picks = []
-    dense = list(range(p.n_head)) + list(range(p.n_head + p.n_sparse, p.n_blocks))
-    for q in (dense[0], dense[-1]):
-        picks.append((0, q, int(rng.integers(heads))))
-    for _ in range(n_sparse):
-        picks.append((0, int(rng.integers(p.n_head, p.n_head + p.n_sparse)),
-                      int(rng.integers(heads))))
-    return sorted(set(picks))
+def _xcd_run_ends(p, batch, heads):
+    """(b, q, n) of the last workgroup of each XCD's contiguous run, in both
+    phases of the attention kernel's dispatch (its workgroup -> block map)."""
+    n_dense = p.n_head + p.n_tail
+    out = []
+    for total, dense in ((batch * heads * n_dense, True), (batch * heads * p.n_sparse, False)):
+        if total == 0:
+            continue
+        per, rem = divmod(total, XCDS)
+        for x in range(XCDS):
+            end = (x + 1) * per + min(x + 1, rem) - 1
+            if end < 0 or end >= total:
+                continue
+            if dense:
+                bn, qd = divmod(end, n_dense)
+                q = qd if qd < p.n_head else qd + p.n_sparse
+            else:
+                bn, qs = divmod(end, p.n_sparse)
+                q = p.n_head + qs
+            out.append((bn // heads, q, bn % heads))
+    return out
+
+
+def _pairs(p, batch, heads, full):
+    if full:
+        return [(b, q, n) for b in range(batch) for q in range(p.n_blocks) for n in range(heads)]
+    qs = {0, p.n_blocks - 1} | set(range(p.n_head, p.n_head + p.n_sparse, 16))
+    picks = {(b, q, n) for b in range(batch) for q in qs for n in range(heads)}
+    picks |= set(_xcd_run_ends(p, batch, heads))
+    return sorted(picks)
+
+
+def _dequant(codes, sigma, p, dtype=np.float64):
+    d = np.empty(codes.shape, dtype=dtype)
+    for j, (r0, n) in enumerate(p.blocks):
+        d[:, :, r0:r0 + n] = oracle.e4m3_decode(codes[:, :, r0:r0 + n]) * sigma[:, :, j, None, None]
+    return d
 
 
 @pytest.mark.parametrize("name", [mx_param(n) for n in ("wan22", "minimax_h3", "wan22_mix",
                                                         "wan22_fp8", "wan22_mxfp4", "gqa_long")])
 def test_full_size(name):
+    import torch
     import block_sparse_video_rf_amd as rf
     w = WORKLOADS[name]
     desc = rf.Desc.from_workload(w)
@@ -72,11 +113,26 @@ def test_full_size(name):
     log("  pools within 2e-6")
     scale = 1.0 / np.sqrt(w.head_dim)
     scores = oracle.block_scores(qpool_o, kpool_o, scale)
+    # The block scores the selection ranked: the first piece of the workspace,
+    # fp32 [B, N1, nS, nS], within 1e-5 of each row's largest magnitude.
+    nS = p.n_sparse
+    ws_scores = bufs.workspace[:w.batch * w.heads_q * nS * nS * 4].view(
+        torch.float32).cpu().numpy().reshape(w.batch, w.heads_q, nS, nS)
+    dev = np.abs(ws_scores - scores).max(axis=-1)
+    rel = dev / np.abs(scores).max(axis=-1)
+    log(f"  block scores: worst row deviation {rel.max():.2e} of the row's largest magnitude")
+    assert rel.max() <= 1e-5
     gi = bufs.select_idx.cpu().numpy()
     gn = bufs.select_num.cpu().numpy()
     swaps = check_selection(p, w.batch, w.heads_q, gi, gn, scores)
     log(f"  selection exact ({swaps} near-tie rows)")
+    if name.startswith("wan22"):
+        _LISTS[name] = (gi, gn)
+        if "wan22" in _LISTS and name != "wan22":
+            assert np.array_equal(gi, _LISTS["wan22"][0]) and np.array_equal(gn, _LISTS["wan22"][1])
+            log("  selectIdx / selectNum identical to the bf16 workload's")
     q_att, k_att = f32(qp_o), f32(kp_o)
+    arrays = dict(q=q_att, k=k_att, v=f32(vp_o))
     if w.precision in ("mix", "fp8"):
         q8, sq = oracle.quantize_blocks(q_att, p)
         k8, sk = oracle.quantize_blocks(k_att, p)
@@ -85,76 +141,66 @@ def test_full_size(name):
         assert np.array_equal(bufs.q_scale.cpu().numpy(), sq)
         assert np.array_equal(bufs.k_scale.cpu().numpy(), sk)
         log("  fp8 codes and scales bit-exact")
+        arrays.update(qd=_dequant(q8, sq, p), kd=_dequant(k8, sk, p))
+        if w.precision == "fp8":
+            arrays["vd"] = _dequant(v8, sv, p, np.float32)   # power-of-two scales: exact
     if w.precision == "mxfp4":
-        q4, eq = oracle.quantize_rows_mx(q_att)
-        k4, ek = oracle.quantize_rows_mx(k_att)
-        assert np.array_equal(unpack_e2m1(bufs.q8.cpu().numpy()), q4)
-        assert np.array_equal(unpack_e2m1(bufs.k8.cpu().numpy()), k4)
-        assert np.array_equal(bufs.q_scale.cpu().numpy(), (eq + 127).astype(np.uint8))
-        assert np.array_equal(bufs.k_scale.cpu().numpy(), (ek + 127).astype(np.uint8))
-        log("  mxfp4 codes and scales bit-exact")
-        qdq = oracle.dequantize_rows_mx(q4, eq)
-        kdq = oracle.dequantize_rows_mx(k4, ek)
-        vdq = oracle.dequantize_v_mx(v4, ev, p)
-        errs_same, errs_own, errs_dev = [], [], []
-    rng = np.random.default_rng(11)
-    picks = _samples(p, w.heads_q, rng)
+        _mxfp4_attention(w, p, pi, res, gi, gn, q_att, k_att, f32(vp_o), v4, ev, scale)
+        return
+    # The GPU's output back in permuted order, so each pair is a block of rows.
+    arrays["out"] = oracle.permute_rows(f32(to_host_u16(res["out"])), pi)
+    full = name == "minimax_h3"
+    pairs = _pairs(p, w.batch, w.heads_q, full)
+    log(f"  attention: {len(pairs)} (query block, head) pairs of {w.batch * p.n_blocks * w.heads_q}"
+        f"{' (the whole output)' if full else ''}")
+    mode = {"bf16": "bf16", "mix": "mix", "fp8": "fp8"}[w.precision]
+    tol = MIX_TOL if mode == "mix" else BF16_TOL
+    results = compare_pairs(arrays, p.blocks, pairs, (gi, gn), scale, w.heads_q // w.heads_kv,
+                            mode, tol=tol, kernel_tol=BF16_TOL)
+    bad = [r["pair"] for r in results if not r["ok"]]
+    n = sum(r["n"] for r in results)
+    worst = max(r["max"] for r in results)
+    mean = sum(r["sum"] for r in results) / n
+    msg = f"  end to end: {n} outputs, max-abs {worst:.3e}, mean-abs {mean:.3e}"
+    if mode != "bf16":
+        msg += (f"; against the {mode} reading max-abs {max(r['same_max'] for r in results):.3e}, "
+                f"mean-abs {sum(r['same_sum'] for r in results) / n:.3e}")
+    if mode == "fp8":
+        msg += f", worst err/bound {max(r['ratio'] for r in results):.3f}"
+    log(msg)
+    assert not bad, bad[:10]
+    assert mean <= (MIX_TOL if mode == "mix" else BF16_TOL)[1] or mode == "fp8"
+
+
+def _mxfp4_attention(w, p, pi, res, gi, gn, q_att, k_att, vp_f, v4, ev, scale):
+    """mxfp4: sampled pairs against the oracle's mxfp4 reading on the same codes,
+    and end to end no further from the unquantised result than that reading."""
+    q4, eq = oracle.quantize_rows_mx(q_att)
+    k4, ek = oracle.quantize_rows_mx(k_att)
+    qdq = oracle.dequantize_rows_mx(q4, eq)
+    kdq = oracle.dequantize_rows_mx(k4, ek)
+    vdq = oracle.dequantize_v_mx(v4, ev, p)
     out_nat = f32(to_host_u16(res["out"]))
-    vp_f = f32(vp_o)
     G = w.heads_q // w.heads_kv
-    worst = [0.0, 0.0]
-    for b, qb, n in picks:
+    errs_same, errs_own, errs_dev = [], [], []
+    for b, qb, n in _pairs(p, w.batch, w.heads_q, False)[::8]:
         r0, m = p.blocks[qb]
         ids = gi[qb, n, :gn[qb, n]]
         rows = oracle.attention.listed_rows(p, ids)
-        refs = []
-        if w.precision == "mxfp4":
-            got = out_nat[b, n, pi[r0:r0 + m]].astype(np.float64)
-            ref = oracle.attention_block_mxp(qdq[b, n, r0:r0 + m], kdq[b, n // G, rows],
-                                             vdq[b, n // G, rows], scale,
-                                             oracle.attention.listed_groups(p, ids))
-            exact = oracle.attention_block(q_att[b, n, r0:r0 + m], k_att[b, n // G, rows],
-                                           vp_f[b, n // G, rows], scale)
-            errs_same.append(np.abs(got - ref).ravel())
-            errs_own.append(np.abs(ref - exact).ravel())
-            errs_dev.append(np.abs(got - exact).ravel())
-            continue
-        if w.precision in ("mix", "fp8"):
-            def deq(codes, sig):
-                return np.concatenate([oracle.e4m3_decode(codes[b, n // G, p.blocks[j][0]:
-                                                                p.blocks[j][0] + p.blocks[j][1]])
-                                       * sig[b, n // G, j] for j in ids])
-            qd = oracle.e4m3_decode(q8[b, n, r0:r0 + m]) * sq[b, n, qb]
-            kd = deq(k8, sk)
-            exact = oracle.attention_block(q_att[b, n, r0:r0 + m], k_att[b, n // G, rows],
-                                           vp_f[b, n // G, rows], scale)
-            if w.precision == "mix":
-                refs.append((oracle.attention_block(qd, kd, vp_f[b, n // G, rows], scale),
-                             BF16_TOL))
-                refs.append((exact, MIX_TOL))
-            else:
-                refs.append((oracle.attention_block_fp8p(qd, kd, deq(v8, sv), scale), FP8_TOL))
-                refs.append((exact, FP8_E2E_TOL))
-        else:
-            refs.append((oracle.attention_block(q_att[b, n, r0:r0 + m], k_att[b, n // G, rows],
-                                                vp_f[b, n // G, rows], scale), BF16_TOL))
-        got = out_nat[b, n, pi[r0:r0 + m]]  # through the inverse arrangement
-        for ref, tol in refs:
-            err = np.abs(got.astype(np.float64) - ref)
-            assert err.max() <= tol[0] and err.mean() <= tol[1], (b, qb, n, err.max(), err.mean())
-            worst = [max(worst[0], err.max()), max(worst[1], err.mean())]
-    if w.precision == "mxfp4":
-        # Over all sampled blocks: the mxfp4 bound against the oracle's reading
-        # on the same codes, and end to end no further from the unquantised
-        # result than the oracle's own mxfp4 output is.
-        e_same = np.concatenate(errs_same)
-        frac = float((e_same > BF16_TOL[0]).mean())
-        own, dev = np.concatenate(errs_own), np.concatenate(errs_dev)
-        log(f"  attention on {len(picks)} sampled blocks: max-abs {e_same.max():.3e} mean-abs "
-            f"{e_same.mean():.3e} beyond-bf16 {frac:.2e}; end to end mean {dev.mean():.3e} "
-            f"(oracle mxfp4 {own.mean():.3e})")
-        assert e_same.max() <= MXFP4_TOL[0] and e_same.mean() <= MXFP4_TOL[1] and frac <= 5e-3
-        assert dev.mean() <= 1.05 * own.mean() + 1e-4
-        return
-    log(f"  attention on {len(picks)} sampled blocks: worst max-abs {worst[0]:.3e} "
-        f"mean-abs {worst[1]:.3e}")
+        got = out_nat[b, n, pi[r0:r0 + m]].astype(np.float64)
+        ref = oracle.attention_block_mxp(qdq[b, n, r0:r0 + m], kdq[b, n // G, rows],
+                                         vdq[b, n // G, rows], scale,
+                                         oracle.attention.listed_groups(p, ids))
+        exact = oracle.attention_block(q_att[b, n, r0:r0 + m], k_att[b, n // G, rows],
+                                       vp_f[b, n // G, rows], scale)
+        errs_same.append(np.abs(got - ref).ravel())
+        errs_own.append(np.abs(ref - exact).ravel())
+        errs_dev.append(np.abs(got - exact).ravel())
+    e_same = np.concatenate(errs_same)
+    frac = float((e_same > BF16_TOL[0]).mean())
+    own, dev = np.concatenate(errs_own), np.concatenate(errs_dev)
+    log(f"  attention on {len(errs_same)} sampled blocks: max-abs {e_same.max():.3e} mean-abs "
+        f"{e_same.mean():.3e} beyond-bf16 {frac:.2e}; end to end mean {dev.mean():.3e} "
+        f"(oracle mxfp4 {own.mean():.3e})")
+    assert e_same.max() <= MXFP4_TOL[0] and e_same.mean() <= MXFP4_TOL[1] and frac <= 5e-3
+    assert dev.mean() <= 1.05 * own.mean() + 1e-4

@@ -7,9 +7,9 @@ from .rf import (Buffers, Desc, RfError, RfPlanInfo, attention, dense_attention,
                  rf_dense_attn, rf_permute, rf_plan, rf_pool_select, rf_pool_select_noalloc,
                  rf_sparse_attn, NOALLOC_SCRATCH_BYTES,
                  rf_status_str, rf_unpermute, rf_version, EXPORTS, LIB_PATH)
-from .schedule import DenseSchedule, QuantSkips, parse_layers, route, scheduled_attention
+from .schedule import DenseSchedule, parse_layers, route, scheduled_attention
 
-__all__ = ["Buffers", "DenseSchedule", "QuantSkips", "route", "Desc", "RfError", "RfPlanInfo", "attention",
+__all__ = ["Buffers", "DenseSchedule", "route", "Desc", "RfError", "RfPlanInfo", "attention",
            "dense_attention", "load_library", "parse_layers", "rf_dense_attn", "rf_permute",
            "rf_plan", "rf_pool_select", "rf_pool_select_noalloc", "rf_sparse_attn",
            "NOALLOC_SCRATCH_BYTES", "rf_status_str", "rf_unpermute",

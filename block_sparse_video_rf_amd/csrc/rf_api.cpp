@@ -21,10 +21,9 @@ namespace {
 
 bool valid_layout(int32_t l) { return l == RF_LAYOUT_BNSD || l == RF_LAYOUT_TND; }
 
-// The mxfp4 kernels are built but switched off until they have passed their
-// parity check on the hardware: the device entry points refuse the precision
-// with RF_ERR_UNSUPPORTED, and rf_plan still reports its buffer sizes.
-constexpr bool kMxfp4Enabled = false;
+// Switch for the mxfp4 kernels: when false the device entry points refuse the
+// precision with RF_ERR_UNSUPPORTED (rf_plan still reports its buffer sizes).
+constexpr bool kMxfp4Enabled = true;
 bool mxfp4_off(const rf_desc* d) { return d->precision == RF_PREC_MXFP4 && !kMxfp4Enabled; }
 
 // [a, a+na) and [b, b+nb) overlap (both non-empty, both non-null).
@@ -364,8 +363,7 @@ const char* rf_status_str(rf_status status) {
     case RF_ERR_GEOMETRY: return "video grid, prefix or first-frame rows inconsistent with seq_len";
     case RF_ERR_WORKSPACE: return "workspace smaller than rf_plan requires";
     case RF_ERR_UNSUPPORTED: return "valid but not supported by the library (block shape 128x128, "
-                                    "head_dim 64/128, <= 8192 sparse blocks; mxfp4 kernels are "
-                                    "switched off)";
+                                    "head_dim 64/128, <= 8192 sparse blocks)";
     case RF_ERR_PRECISION: return "unknown precision, or a buffer that precision needs is NULL";
     case RF_ERR_HIP: return "HIP launch failed";
     case RF_ERR_ALIAS: return "an output buffer overlaps an input buffer";

@@ -114,10 +114,7 @@ typedef enum rf_precision {
                        (any integer M gives the same result), out = sum P v / sum P
                        ([MXA]). No rotation
                        ([RFA] mentions a default rotation policy without defining it).
-                       Softmax bookkeeping and accumulation fp32, output bf16.
-                       At present rf_permute, rf_sparse_attn and rf_dense_attn return
-                       RF_ERR_UNSUPPORTED for it (its kernels are built but have not yet
-                       passed their check on the hardware); rf_plan reports its sizes. */
+                       Softmax bookkeeping and accumulation fp32, output bf16. */
 } rf_precision;
 
 /* One attention call. Sizes are per batch item; all batch items share the

@@ -49,20 +49,19 @@ from synth import bf16_to_f32, from_tnd, make_qkv, to_tnd
 # to w/2 * max|v - O|), and at most 0.5% of the outputs may exceed the bf16 max
 # bound.
 MXFP4_TOL = (0.25, 2e-3)
-# The library refuses mxfp4 in its device entry points for now (RF_ERR_UNSUPPORTED):
-# the mxfp4 attention kernel faulted the GPU on its first runs (it read the fp8
-# block scale through a pointer that is unset in mxfp4; fixed on the CPU side,
-# shown in the compiled code), and the fixed kernels have not had their check on
-# the hardware yet.
-MXFP4_SKIP = ("mxfp4 kernels switched off: they faulted the GPU on their first runs (null fp8 "
-              "block-scale pointer read in mxfp4, since fixed); re-enabled after the fix passes "
-              "its hardware check")
+# mxfp4 GPU cases run only while the library's mxfp4 kernels are switched on
+# (rf_api.cpp); otherwise they are skipped with this reason.
+MXFP4_ENABLED = True
+MXFP4_SKIP = ("mxfp4 kernels switched off in the library (rf_api.cpp kMxfp4Enabled)")
 
 
 def mx_param(name):
-    """A parametrize value, skipped (with the reason) if it runs the mxfp4 kernels."""
+    """A parametrize value, skipped (with the reason) if it runs the mxfp4 kernels
+    while they are switched off."""
     import pytest
-    return pytest.param(name, marks=pytest.mark.skip(reason=MXFP4_SKIP)) if "mxfp4" in name else name
+    if "mxfp4" in name and not MXFP4_ENABLED:
+        return pytest.param(name, marks=pytest.mark.skip(reason=MXFP4_SKIP))
+    return name
 BF16_TOL = (2e-2, 2e-3)
 MIX_TOL = (6e-2, 6e-3)
 NEAR_TIE_REL = 1e-5

@@ -140,9 +140,9 @@ def test_invalid_descriptors(name, change, status):
     assert lib.rf_unpermute(ctypes.byref(c), fake, fake, None) == status
 
 
-def test_mxfp4_sizes_planned_and_device_entry_points_refused():
-    """rf_plan reports the mxfp4 buffer sizes; the device entry points refuse the
-    precision (RF_ERR_UNSUPPORTED) before any launch while its kernels are off."""
+def test_mxfp4_sizes_planned_and_buffers_checked():
+    """rf_plan reports the mxfp4 buffer sizes; the device entry points check the
+    buffers mxfp4 needs before any launch (RF_ERR_PRECISION without them)."""
     d = _good()
     d.precision = "mxfp4"
     info = rf.rf_plan(d)
@@ -157,13 +157,16 @@ def test_mxfp4_sizes_planned_and_device_entry_points_refused():
     lib = load_library()
     c = d.c()
     fake = ctypes.c_void_p(1 << 40)
+    # Q without its E8M0 scales; V without its scales; attention without V scales.
     assert lib.rf_permute(ctypes.byref(c), fake, None, None, None, None, None, None, None,
-                          ctypes.c_void_p(2 << 40), None, ctypes.c_void_p(3 << 40), None, None,
-                          None) == 10
-    assert lib.rf_sparse_attn(ctypes.byref(c), None, None, fake, fake, fake, fake, fake, fake,
-                              fake, fake, info.n_blocks, ctypes.c_void_p(5 << 40), None) == 10
-    assert lib.rf_dense_attn(ctypes.byref(c), None, None, fake, fake, fake, fake, fake, fake,
-                             ctypes.c_void_p(5 << 40), None) == 10
+                          ctypes.c_void_p(2 << 40), None, None, None, None, None) == 11
+    assert lib.rf_permute(ctypes.byref(c), None, None, fake, None, None,
+                          ctypes.c_void_p(2 << 40), None, None, None, None, None, None, None,
+                          None) == 11
+    assert lib.rf_sparse_attn(ctypes.byref(c), None, None, fake, fake, fake, fake, fake, None,
+                              fake, fake, info.n_blocks, ctypes.c_void_p(5 << 40), None) == 11
+    assert lib.rf_dense_attn(ctypes.byref(c), None, None, fake, fake, fake, fake, fake, None,
+                             ctypes.c_void_p(5 << 40), None) == 11
     # Per-precision sizes of the other modes.
     for prec, q8, vpt in (("bf16", 0, 2), ("mix", 1, 2), ("fp8", 1, 1)):
         d.precision = prec

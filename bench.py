@@ -53,7 +53,7 @@ def parse_args():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for HBM counter calibration)")
     ap.add_argument("--peaks", action="store_true",
-                    help="only measure the achievable peaks: an MFMA microbenchmark (bf16, fp8), "
+                    help="only measure the achievable peaks: an MFMA microbenchmark (bf16, fp8), an LDS / VALU microbenchmark, "
                          "a large bf16 GEMM (hipBLASLt) and a "
                          "device-to-device copy")
     return ap.parse_args()
@@ -98,7 +98,16 @@ def measure_peaks(torch, dev):
                     "bf16_frac_of_published": round(m["mfma_bf16_tflops"] / PEAK_TFLOPS["bf16"], 3),
                     "fp8_tflops": m["mfma_fp8_tflops"],
                     "fp8_frac_of_published": round(m["mfma_fp8_tflops"] / PEAK_TFLOPS["fp8"], 3)}
-    return {"mfma_microbenchmark": mfma,
+    # LDS bandwidth and vector-ALU issue costs in shader cycles
+    # (tests/native/lds_valu_peak).
+    lds_valu = None
+    exe = os.path.join(ROOT, "tests", "native", "lds_valu_peak")
+    if os.path.exists(exe):
+        import subprocess
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+        if r.returncode == 0:
+            lds_valu = json.loads(r.stdout.strip().splitlines()[-1])
+    return {"mfma_microbenchmark": mfma, "lds_valu_microbenchmark": lds_valu,
             "gemm_bf16": {"m": n, "n": n, "k": n, "ms": round(gemm_ms, 4),
                           "tflops": round(2.0 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
                           "frac_of_published": round(2.0 * n ** 3 / (gemm_ms * 1e-3) / 1e12

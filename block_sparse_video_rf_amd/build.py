@@ -68,13 +68,18 @@ def build(verbose: bool = False) -> str:
 
 
 def build_mfma_peak() -> str:
-    """Compile the matrix-core microbenchmark that bench.py --peaks runs."""
-    src = os.path.join(os.path.dirname(PKG), "tests", "native", "mfma_peak.cpp")
-    exe = os.path.join(os.path.dirname(src), "mfma_peak")
-    if not os.path.exists(src):
-        return ""
-    _run([HIPCC, *HIP_FLAGS, src, "-o", exe])
-    return exe
+    """Compile the microbenchmarks that bench.py --peaks runs: the matrix-core
+    rate (mfma_peak) and the LDS bandwidth / vector-ALU issue costs
+    (lds_valu_peak). Returns the first program's path."""
+    native = os.path.join(os.path.dirname(PKG), "tests", "native")
+    built = []
+    for name in ("mfma_peak", "lds_valu_peak"):
+        src = os.path.join(native, name + ".cpp")
+        if os.path.exists(src):
+            exe = os.path.join(native, name)
+            _run([HIPCC, *HIP_FLAGS, src, "-o", exe])
+            built.append(exe)
+    return built[0] if built else ""
 
 
 def build_abi_check() -> str:

@@ -36,7 +36,6 @@ METRIC = "sparse attn ms/call + dense-equiv TFLOPS & MFMA util at 0.8 sparsity, 
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
 HBM_PEAK_GBS = 8000.0
 ATTN_SRC = os.path.join(ROOT, "block_sparse_video_rf_amd", "csrc", "rf_attn.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_kernel_wan22_pmc.txt")
 
 
 def parse_args():
@@ -135,14 +134,21 @@ def listed_key_rows(select_idx, select_num, lengths):
     return np.where(valid, lengths[np.clip(idx, 0, None)], 0).sum(axis=-1)
 
 
-def traffic_from_profile():
-    """HBM bytes per launch of the attention kernel from the committed counter summary,
-    or None when it is absent or was taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_file(workload):
+    """The committed counter summary of the attention kernel on this workload."""
+    return os.path.join(ROOT, "profiles", f"sparse_attn_kernel_{workload}_pmc.txt")
+
+
+def traffic_from_profile(workload):
+    """HBM bytes per launch of the attention kernel from the committed counter summary
+    of this workload, or None when it is absent or was taken on a different kernel
+    source."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
     want = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line:
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
@@ -434,7 +440,7 @@ def main():
         hbm["pool_select"].update(counter_bytes=cb, counter_GB_s=round(cb / select_ms / 1e6, 1),
                                   counter_frac_of_peak=round(cb / select_ms / 1e6 / HBM_PEAK_GBS, 3))
 
-    traffic = traffic_from_profile()
+    traffic = traffic_from_profile(args.workload)
     result = {
         "metric": METRIC,
         "value": round(attn_ms, 4),

@@ -48,13 +48,15 @@ def test_listed_key_rows_hand_made():
     assert got.tolist() == [[160, 100], [260, 32]]
 
 
-def test_traffic_needs_the_profiled_kernel_source(tmp_path, monkeypatch):
-    if not os.path.exists(bench.TRAFFIC_FILE):
-        pytest.skip("no counter summary committed")
+@pytest.mark.parametrize("workload", ["wan22", "wan22_mix", "wan22_fp8", "wan22_mxfp4"])
+def test_traffic_needs_the_profiled_kernel_source(tmp_path, monkeypatch, workload):
+    path = bench.traffic_file(workload)
+    if not os.path.exists(path):
+        pytest.skip("no counter summary committed for " + workload)
     vals = {k.strip(): v.strip() for k, v in
-            (line.split(":", 1) for line in open(bench.TRAFFIC_FILE) if ":" in line)}
+            (line.split(":", 1) for line in open(path) if ":" in line)}
     current = hashlib.sha256(open(bench.ATTN_SRC, "rb").read()).hexdigest()
-    got = bench.traffic_from_profile()
+    got = bench.traffic_from_profile(workload)
     if vals.get("source_sha256") == current:
         assert got == pytest.approx(float(vals["traffic_bytes_per_launch"]))
     else:
@@ -64,7 +66,7 @@ def test_traffic_needs_the_profiled_kernel_source(tmp_path, monkeypatch):
     with open(src, "a") as f:
         f.write("\n// changed\n")
     monkeypatch.setattr(bench, "ATTN_SRC", str(src))
-    assert bench.traffic_from_profile() is None
+    assert bench.traffic_from_profile(workload) is None
 
 
 def test_more_than_one_gpu_is_refused():

@@ -37,18 +37,8 @@ import oracle
 from oracle.geometry import Geometry, permutation, plan
 from synth import bf16_to_f32, from_tnd, make_qkv, to_tnd
 
-# mxfp4 against the oracle's mxfp4 reading on the same codes: the kernel takes
-# logits and exponentials in fp32, the oracle in float64, so a P next to an E2M1
-# rounding midpoint (or a block maximum next to 7.25 * 2^e) can land on the
-# neighbouring code: one E2M1 step, up to half of that P. A CPU simulation of the
-# kernel's one-pass fp32 arithmetic (running integer reference, per-lane 32-key
-# MX blocks, exp2 with 1-ulp noise) against the oracle on the small cases gives
-# max 5.6e-3, mean 1.1e-4 and no element beyond 2e-2 (3.4M, 0.6M and 3.1M
-# outputs). The mean bound is the bf16 one; the max bound leaves room for one
-# flipped P in a short, peaked row (a share w of the row moves the output by up
-# to w/2 * max|v - O|), and at most 0.5% of the outputs may exceed the bf16 max
-# bound.
-MXFP4_TOL = (0.25, 2e-3)
+# fp8 and mxfp4 against the oracle's reading on the same codes: the derived
+# per-element bounds of tests/fp8_bounds.py (kernel_bound, mx_kernel_bound).
 # mxfp4 GPU cases run only while the library's mxfp4 kernels are switched on
 # (rf_api.cpp); otherwise they are skipped with this reason.
 MXFP4_ENABLED = True
@@ -167,18 +157,6 @@ def attention_error(gpu_out_f32, ref):
     return float(err.max()), float(err.mean())
 
 
-def assert_close_mx(gpu_out_f32, ref, tol, what="", frac_max=5e-3):
-    """mxfp4: max-abs and mean-abs as assert_close, and at most ``frac_max`` of
-    the elements outside the bf16 max-abs bound (a P code that flips at an E2M1
-    rounding midpoint moves its row; all other rows match to bf16 rounding)."""
-    err = np.abs(gpu_out_f32.astype(np.float64) - ref)
-    mx, mean = float(err.max()), float(err.mean())
-    frac = float((err > BF16_TOL[0]).mean())
-    log(f"  {what} max-abs {mx:.3e} mean-abs {mean:.3e} beyond-bf16 {frac:.2e} "
-        f"(tol {tol[0]:.0e}/{tol[1]:.0e}/{frac_max:.0e})")
-    assert mx <= tol[0] and mean <= tol[1] and frac <= frac_max, (what, mx, mean, frac)
-
-
 def assert_close(gpu_out_f32, ref, tol, what=""):
     mx, mean = attention_error(gpu_out_f32, ref)
     log(f"  {what} max-abs {mx:.3e} mean-abs {mean:.3e} (tol {tol[0]:.0e}/{tol[1]:.0e})")
@@ -199,14 +177,22 @@ def _dequant_blocks(codes, sigma, p):
 
 def fp8_bound_permuted(ores, select):
     """Per-element bound [B, N1, S, D] (permuted rows) of |GPU - oracle| in fp8
-    precision: tests/fp8_bounds.kernel_bound for every (batch, query block,
-    head) over the blocks ``select`` lists, on the oracle's own E4M3 operands
-    (``ores``: an ``oracle.run(..., precision="fp8")`` result)."""
-    from fp8_bounds import kernel_bound
+    or mxfp4 precision: tests/fp8_bounds.kernel_bound (fp8) or mx_kernel_bound
+    (mxfp4) for every (batch, query block, head) over the blocks ``select``
+    lists, on the oracle's own quantised operands (``ores``: an
+    ``oracle.run(..., precision="fp8" or "mxfp4")`` result)."""
+    from fp8_bounds import kernel_bound, mx_kernel_bound
     p = ores["plan"]
-    qd = _dequant_blocks(ores["q8"], ores["q_scale"], p)
-    kd = _dequant_blocks(ores["k8"], ores["k_scale"], p)
-    vd = _dequant_blocks(ores["v8"], ores["v_scale"], p)
+    if "q4" in ores:
+        bound = mx_kernel_bound
+        qd = oracle.dequantize_rows_mx(ores["q4"], ores["q_exp"])
+        kd = oracle.dequantize_rows_mx(ores["k4"], ores["k_exp"])
+        vd = oracle.dequantize_v_mx(ores["v4"], ores["v_exp"], p)
+    else:
+        bound = kernel_bound
+        qd = _dequant_blocks(ores["q8"], ores["q_scale"], p)
+        kd = _dequant_blocks(ores["k8"], ores["k_scale"], p)
+        vd = _dequant_blocks(ores["v8"], ores["v_scale"], p)
     idx, num = select
     B, N1, S, D = qd.shape
     G = N1 // kd.shape[1]
@@ -216,9 +202,11 @@ def fp8_bound_permuted(ores, select):
             r0, m = p.blocks[q]
             row = b * p.n_blocks + q
             for n in range(N1):
-                rows = oracle.attention.listed_rows(p, idx[row, n, :num[row, n]])
-                out[b, n, r0:r0 + m] = kernel_bound(qd[b, n, r0:r0 + m], kd[b, n // G, rows],
-                                                    vd[b, n // G, rows], ores["scale"])
+                ids = idx[row, n, :num[row, n]]
+                rows = oracle.attention.listed_rows(p, ids)
+                out[b, n, r0:r0 + m] = bound(qd[b, n, r0:r0 + m], kd[b, n // G, rows],
+                                             vd[b, n // G, rows], ores["scale"],
+                                             oracle.attention.listed_groups(p, ids))
     return out
 
 
@@ -328,17 +316,7 @@ def full_check(w, extra, name=None):
     ref_same_sel = same["out"]
     bf16_ref = ores["out"] if w.precision == "bf16" else oracle.run(
         f32(q), f32(k), f32(v), g, layout=layout, batch=w.batch)["out"]
-    if w.precision == "mxfp4":
-        assert_close_mx(out, ref_same_sel, MXFP4_TOL, "attention (GPU lists)")
-        # End to end: MXFP4 is coarse, so the bar is the oracle's own mxfp4
-        # deviation from the unquantised result on the same inputs.
-        own = np.abs(ores["out"] - bf16_ref)
-        dev = np.abs(out.astype(np.float64) - bf16_ref)
-        log(f"  end to end vs bf16 oracle: mean-abs {dev.mean():.3e} (oracle mxfp4 {own.mean():.3e}), "
-            f"max-abs {dev.max():.3e} (oracle {own.max():.3e})")
-        assert dev.mean() <= 1.05 * own.mean() + 1e-4
-        assert dev.max() <= own.max() + MXFP4_TOL[0]
-    elif w.precision == "fp8":
+    if w.precision in ("fp8", "mxfp4"):
         # The derived per-element bound against the reading on the GPU's lists;
         # end to end, no further from the unquantised result than the reading.
         kb = in_output_layout(fp8_bound_permuted(same, (gi, gn)), same, layout, w.batch)

@@ -15,14 +15,16 @@ Comparison per pair (``mode``):
 * ``mix``: the GPU against the oracle on dequantised Q/K (``kernel_tol``), and
   against the exact oracle within the mix bound, or within the quantised
   reading's own deviation plus ``kernel_tol`` where that is larger;
-* ``fp8``: the GPU against the fp8 reading on the same codes within the
-  derived per-element bound (tests/fp8_bounds.py), and against the exact
-  oracle within the reading's own deviation plus that bound.
+* ``fp8``, ``mxfp4``: the GPU against the fp8 (mxfp4) reading on the same
+  codes within the derived per-element bound (tests/fp8_bounds.py), and
+  against the exact oracle within the reading's own deviation plus that
+  bound.
 """
 from __future__ import annotations
 
 import os
 import tempfile
+import types
 from concurrent.futures import ProcessPoolExecutor
 from multiprocessing import get_context
 
@@ -44,7 +46,7 @@ def _rows(ids):
 
 def _pair(b, q, n, ids):
     import oracle
-    from fp8_bounds import kernel_bound
+    from fp8_bounds import kernel_bound, mx_kernel_bound
     W = _W
     r0, m = W["blocks"][q]
     G, scale, mode = W["G"], W["scale"], W["mode"]
@@ -70,8 +72,13 @@ def _pair(b, q, n, ids):
                          and err.mean() <= max(tol[1], own.mean() + kt[1]))
         return res
     vd = W["vd"][b, n // G, rows]
-    reading = oracle.attention_block_fp8p(qd, kd, vd, scale)
-    bound = kernel_bound(qd, kd, vd, scale)
+    groups = oracle.attention.listed_groups(types.SimpleNamespace(blocks=W["blocks"]), ids)
+    if mode == "mxfp4":
+        reading = oracle.attention_block_mxp(qd, kd, vd, scale, groups)
+        bound = mx_kernel_bound(qd, kd, vd, scale, groups)
+    else:
+        reading = oracle.attention_block_fp8p(qd, kd, vd, scale)
+        bound = kernel_bound(qd, kd, vd, scale, groups)
     e_same = np.abs(got - reading)
     own = np.abs(reading - exact)
     res.update(same_max=float(e_same.max()), same_sum=float(e_same.sum()),
@@ -90,7 +97,7 @@ def compare_pairs(arrays, blocks, pairs, lists, scale, G, mode, tol=None, kernel
 
     ``arrays``: ``out`` (GPU output, permuted rows, float32 ``[B, N1, S, D]``),
     ``q``, ``k``, ``v`` (permuted inputs), and for ``mix`` ``qd``, ``kd``
-    (dequantised Q/K), for ``fp8`` also ``vd``. ``lists``: (select_idx,
+    (dequantised Q/K), for ``fp8`` and ``mxfp4`` also ``vd``. ``lists``: (select_idx,
     select_num). Returns the per-pair results (dicts with ``ok``)."""
     idx, num = lists
     nB = len(blocks)

@@ -16,8 +16,8 @@ import oracle
 from oracle.geometry import plan, permutation
 from synth import WORKLOADS, Workload, make_qkv, to_tnd, from_tnd
 
-from gpu_harness import (BF16_TOL, MIX_TOL, MXFP4_TOL, assert_close, assert_within,
-                         assert_close_mx, check_selection, expected_vpt, f32, fp8_bound_permuted,
+from gpu_harness import (BF16_TOL, MIX_TOL, assert_close, assert_within,
+                         check_selection, expected_vpt, f32, fp8_bound_permuted,
                          geometry_of, in_output_layout, log,
                          mx_param, mx_v_scale_natural, run_gpu, to_host_u16, unpack_e2m1,
                          case_desc, case_inputs, full_check)
@@ -147,11 +147,10 @@ def test_handmade_lists_skip_invalid_entries(precision):
     ores = oracle.run(f32(q), f32(k), f32(v), g, precision=precision,
                       select=(valid_idx, valid_num))
     ref = ores["out_p"]
-    if precision == "mxfp4":
-        assert_close_mx(f32(to_host_u16(out_p)), ref, MXFP4_TOL, "handmade lists (mxfp4)")
-    elif precision == "fp8":
+    if precision in ("fp8", "mxfp4"):
         assert_within(f32(to_host_u16(out_p)), ref,
-                      fp8_bound_permuted(ores, (valid_idx, valid_num)), "handmade lists (fp8)")
+                      fp8_bound_permuted(ores, (valid_idx, valid_num)),
+                      f"handmade lists ({precision})")
     else:
         assert_close(f32(to_host_u16(out_p)), ref, BF16_TOL, f"handmade lists ({precision})")
 
@@ -236,14 +235,10 @@ def test_reference_raised_mid_row(precision):
     # would show in the mean, which keeps its bound. fp8: the derived
     # per-element bound (peaked rows carry large P shares, so a flipped code or
     # the one-pass subnormal rounding weighs more there; the bound follows).
-    if precision == "mxfp4":
-        assert_close_mx(f32(to_host_u16(res["out"])), ref, MXFP4_TOL, "raised mid-row (mxfp4)",
-                        frac_max=2e-2)
-        return
-    if precision == "fp8":
+    if precision in ("fp8", "mxfp4"):
         kb = in_output_layout(fp8_bound_permuted(ores, (ores["select_idx"], ores["select_num"])),
                               ores)
-        assert_within(f32(to_host_u16(res["out"])), ref, kb, "raised mid-row (fp8)")
+        assert_within(f32(to_host_u16(res["out"])), ref, kb, f"raised mid-row ({precision})")
         return
     assert_close(f32(to_host_u16(res["out"])), ref, (4e-2, BF16_TOL[1]),
                  f"raised mid-row ({precision})")

@@ -25,7 +25,7 @@ import math
 import numpy as np
 
 import oracle
-from oracle.attention import attention_block_fp8p, listed_rows
+from oracle.attention import attention_block_fp8p, listed_groups, listed_rows
 from oracle.fp8 import e4m3_decode, e4m3_round
 from oracle.geometry import Geometry, plan
 from synth import WORKLOADS, bf16_to_f32, make_qkv
@@ -103,7 +103,7 @@ def _compare(integer_exponent, key_scale=1.0, round_p=True):
             got = _one_pass(Q, kd[0, n], vd[0, n], p, ids, scale, integer_exponent, round_p)
             err = np.abs(got - ref)
             worst = max(worst, float(err.max()))
-            bound = kernel_bound(Q, kd[0, n, rows], vd[0, n, rows], scale)
+            bound = kernel_bound(Q, kd[0, n, rows], vd[0, n, rows], scale, listed_groups(p, ids))
             ratio = max(ratio, float((err / bound).max()))
     return worst, ratio
 

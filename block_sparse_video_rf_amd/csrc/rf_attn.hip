@@ -276,8 +276,11 @@ struct MfmaCtx {
   int vexp;                       // E8M0 scale of the previous block's V (fp8)
   // mxfp4 E8M0 scale words (byte = scale of one operand lane's 32 values):
   // Q (byte 2 st: k-step st), K per key tile (likewise), V^T of the previous
-  // block (byte e: channel tile e), P^T (byte 0).
-  int qsc, ksc[2], vsc, psc;
+  // block (byte e: channel tile e).
+  int qsc, ksc[2], vsc;
+  // fp8, mxfp4: E8M0 scale of the P^T operand (byte 0): 2^(m_run - m_ref),
+  // times the lane's MX scale in mxfp4.
+  int psc;
   f32x16 osum;                    // fp8, mxfp4: every value is the running row sum of P
 };
 
@@ -387,7 +390,7 @@ __device__ __forceinline__ void mfma_steps(MfmaCtx<D, PREC>& c) {
         constexpr int k1 = 0x38383838;
         const i32x8 ones = {k1, k1, k1, k1, k1, k1, k1, k1};
         c.osum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, c.pf8, c.osum, 0, 0, 0,
-                                                                 127, 0, 127);
+                                                                 127, 0, c.psc);
       }
     } else if constexpr (P::F4) {
       // O^T tile e += V^T (E2M1, scale byte e of vsc) P^T (E2M1, scale psc)
@@ -401,7 +404,7 @@ __device__ __forceinline__ void mfma_steps(MfmaCtx<D, PREC>& c) {
       constexpr int e = M - P::NS_MFMA;
       const i32x8 va = ring_pair<P::NR, P::NS_READ + 2 * e>(c.ring);
       c.o[e] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, c.pf8, c.o[e], 0, 0, 0, c.vexp,
-                                                               0, 127);
+                                                               0, c.psc);
     } else {
       constexpr int pm = M - P::NS_MFMA, tu = pm / P::DT, e = pm % P::DT;
       constexpr int r = P::NS_READ + pm;
@@ -570,10 +573,11 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     for (int u = 0; u < 2; ++u) c.pf16[t][u] = bf16x8{};
   c.pf8 = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
   c.pf4 = i32x4{0, 0, 0, 0};
-  c.psc = 0;
+  c.psc = 127;
   c.vsc = 0;
   c.osum = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
+  float m_ref = -INFINITY;  // fp8, mxfp4: the reference at which O^T and the row sums are held
 
   const int64_t sel_row = ((int64_t)b * g.n_blocks + q) * g.N1 + n;
   const list_ptr list = ALL ? nullptr : (list_ptr)(a.select_idx + sel_row * a.max_kv);
@@ -870,6 +874,16 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
         for (int v = 0; v < 16; ++v) c.osum[v] *= alpha;
       }
     };
+    // fp8, mxfp4: move the accumulation reference (O^T and the row sums).
+    auto rescale_ref = [&](float new_ref, float alpha) {
+      m_ref = new_ref;
+#pragma unroll
+      for (int e = 0; e < DT; ++e)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) c.o[e][v] *= alpha;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) c.osum[v] *= alpha;
+    };
     // While every key so far is masked m_run is -inf; any finite stand-in keeps
     // exp2(-inf - m) at 0 instead of NaN.
     auto ref_neg = [&]() -> float { return -fmaxf(m_run, -1e30f); };
@@ -888,9 +902,20 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
       const float lm = lane_max();
       const float mc = max_halves(lm) * cs - kTop;
       if (__any(mc > m_run)) {
-        const float m_new = fmaxf(m_run, ceilf(mc));
-        rescale(m_new, m_run == -INFINITY ? 0.0f : ldexpf(1.0f, (int)(m_run - m_new)));
+        m_run = fmaxf(m_run, ceilf(mc));
+        // O^T and the row sums accumulate at the integer reference m_ref, not
+        // at m_run: the products scale P back by 2^(m_run - m_ref) through
+        // their P-operand scale, which is exact, so raising m_run costs no
+        // rescale. m_ref moves up to m_run (rescaling by that power of two)
+        // only at the first finite reference and when the gap exceeds 64
+        // binades, far below where the fp32 sums could overflow.
+        const bool rebase = m_ref == -INFINITY ? m_run != -INFINITY : m_run - m_ref > 64.0f;
+        if (__any(rebase)) {
+          const float new_ref = m_run == -INFINITY ? m_ref : m_run;
+          rescale_ref(new_ref, m_ref == -INFINITY ? 0.0f : ldexpf(1.0f, (int)(m_ref - new_ref)));
+        }
       }
+      const int pgap = (m_run == -INFINITY || m_ref == -INFINITY) ? 0 : (int)(m_run - m_ref);
       const float mneg = ref_neg();
       if constexpr (F4) {
         // The lane's MX block: its largest P fixes the exponent e (rf_mx.h);
@@ -907,7 +932,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
           for (int x = 0; x < 8; ++x) p[x] = __builtin_amdgcn_exp2f(fmaf(c.s[t][v0 + x], cs, mneg_e));
           c.pf4[w] = (int)rf_e2m1_pack8(p);
         }
-        c.psc = ep + 127;
+        c.psc = ep + 127 + pgap;
       } else {
       // P as E4M3 codes (round to nearest even; P <= 448), byte 16 t + v
       // of the B operand. The row sum of the rounded values (what multiplies
@@ -923,6 +948,7 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
         c.pf8[w] = pk;
       }
       c.vexp = (int)((__float_as_uint(vscale[j]) >> 23) & 0xffu);
+      c.psc = 127 + pgap;
       }
     } else {
       // bf16 P and fp32 sums hold exponentials far beyond 1, so the reference
@@ -987,12 +1013,12 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
         const i32x8 va = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                           (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
         c.o[e] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, c.pf8, c.o[e], 0, 0, 0, c.vexp,
-                                                                 0, 127);
+                                                                 0, c.psc);
       }
       constexpr int k1 = 0x38383838;
       const i32x8 ones = {k1, k1, k1, k1, k1, k1, k1, k1};
       c.osum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, c.pf8, c.osum, 0, 0, 0, 127,
-                                                               0, 127);
+                                                               0, c.psc);
     } else {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -1007,7 +1033,10 @@ __global__ __launch_bounds__(kThreads8, 1) void sparse_attn_kernel(AttnArgs a) {
     }
   }
   if (kh == 0) lds_barrier();  // matches the kh = 1 group's extra barrier
-  if constexpr (VQ) l_run = c.osum[0];  // the row sum over this wave's keys (any value)
+  if constexpr (VQ) {
+    l_run = c.osum[0];  // the row sum over this wave's keys (any value)
+    m_run = m_ref;      // the reference at which O^T and the row sum are held
+  }
 
 #undef RF_LOAD_K
 #undef RF_STORE_K

@@ -154,16 +154,12 @@ typedef const float __attribute__((address_space(4)))* scale_ptr;
 // maxima (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-// Raw buffer descriptor over [base, base + bytes). The hardware range-checks
-// only the VGPR offset (with the instruction's immediate), not the SGPR
-// offset, and returns zeros for a load past `bytes`. The tile loads put the
-// block offset in the SGPR operand (a VGPR add per load costs 5% in bf16),
-// which is not clamped: that is safe for every tile that ends inside its
-// (batch, kv head)'s rows (all V tiles, and every K tile but the one of a short
-// block at the end of the sequence). That one K tile is loaded with the whole
-// offset in the VGPR operand instead, so its rows past the sequence read zeros
-// and nothing outside the buffer is touched. (Third dword: the raw 32-bit data
-// format used for plain byte-addressed buffers on gfx9.)
+// Raw buffer descriptor over [base, base + bytes). The hardware compares the
+// whole offset of a load (SGPR offset + VGPR offset + immediate) with `bytes`
+// and returns zeros past it (measured on MI355X), so the K tile of a short
+// block at the end of the sequence reads zeros past the sequence and nothing
+// outside the buffer is touched. (Third dword: the raw 32-bit data format used
+// for plain byte-addressed buffers on gfx9.)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }

@@ -11,10 +11,12 @@ Q/K in every precision).
 The attention output ("aclnnRainFusionAttention", Formula, over the listed
 blocks) is compared through the inverse arrangement against the float64
 oracle, spread over worker processes (tests/oracle_pool.py):
-* minimax_h3: every (query block, head) pair, the whole output;
-* the other workloads: every head at its first block, its last block, every
-  16th sparse block, and the query blocks of the last workgroup of each
-  XCD's run in both dispatch phases (dense query blocks first, then sparse).
+* bf16 and mix (wan22, minimax_h3, wan22_mix, gqa_long): every (query block,
+  head) pair, the whole output;
+* fp8 and mxfp4, whose per-element bounds cost far more than the oracle
+  itself: every head at its first block, its last block, every 16th sparse
+  block, and the query blocks of the last workgroup of each XCD's run in
+  both dispatch phases (dense query blocks first, then sparse).
 """
 import numpy as np
 import pytest
@@ -151,7 +153,7 @@ def test_full_size(name):
                       vd=oracle.dequantize_v_mx(v4, ev, p))
     # The GPU's output back in permuted order, so each pair is a block of rows.
     arrays["out"] = oracle.permute_rows(f32(to_host_u16(res["out"])), pi)
-    full = name == "minimax_h3"
+    full = w.precision in ("bf16", "mix")
     pairs = _pairs(p, w.batch, w.heads_q, full)
     log(f"  attention: {len(pairs)} (query block, head) pairs of {w.batch * p.n_blocks * w.heads_q}"
         f"{' (the whole output)' if full else ''}")

@@ -17,6 +17,9 @@ oracle, spread over worker processes (tests/oracle_pool.py):
   itself: every head at its first block, its last block, every 16th sparse
   block, and the query blocks of the last workgroup of each XCD's run in
   both dispatch phases (dense query blocks first, then sparse).
+
+minimax_h3 also runs in the TND layout, which must reproduce the BNSD run bit
+for bit (every intermediate buffer and the output).
 """
 import numpy as np
 import pytest
@@ -174,3 +177,26 @@ def test_full_size(name):
     log(msg)
     assert not bad, bad[:10]
     assert mean <= (MIX_TOL if mode == "mix" else BF16_TOL)[1] or mode in ("fp8", "mxfp4")
+
+
+def test_full_size_tnd_equals_bnsd():
+    """minimax_h3 in the TND layout (the caller's [B*S, N, D] rows): every
+    intermediate buffer and the output, brought back to BNSD, bit-identical to
+    the BNSD run, whose whole output the test above holds to the oracle (the
+    layouts differ only in how rows are addressed)."""
+    import block_sparse_video_rf_amd as rf
+    from synth import from_tnd, to_tnd
+    w = WORKLOADS["minimax_h3"]
+    log(f"[full {w.name} TND] N={w.heads_q}/{w.heads_kv} S={w.seq_len} grid={w.grid}")
+    q, k, v = make_qkv(w)
+    a = run_gpu(rf.Desc.from_workload(w), q, k, v)
+    t = run_gpu(rf.Desc.from_workload(w, layout="TND"), to_tnd(q), to_tnd(k), to_tnd(v))
+    ba, bt = a["bufs"], t["bufs"]
+    for name in ("qp", "kp", "vpt"):
+        assert np.array_equal(to_host_u16(getattr(ba, name)), to_host_u16(getattr(bt, name))), name
+    for name in ("q_pool", "k_pool", "select_idx", "select_num"):
+        assert np.array_equal(getattr(ba, name).cpu().numpy(), getattr(bt, name).cpu().numpy()), name
+    out_a = to_host_u16(a["out"])
+    out_t = from_tnd(to_host_u16(t["out"]), w.batch)
+    assert np.array_equal(out_a, out_t)
+    log(f"  TND: permuted Q/K/V, pools, lists and the {out_a.size} outputs bit-identical to BNSD")

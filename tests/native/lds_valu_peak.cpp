@@ -9,6 +9,12 @@
 // independent register chains of one instruction (v_exp_f32, or v_fma_f32 as
 // the full-rate reference), so the figure is the issue cost of one wave64
 // instruction on its SIMD.
+// Co-issue: one workgroup of 8 waves per CU, waves w and w + 4 on one SIMD;
+// waves 0..3 issue four independent chains of one MFMA (bf16 32x32x16 or the
+// scaled fp8 32x32x64) from registers, waves 4..7 sixteen independent vector
+// chains per round (16 FMAs, or 8 FMAs and 8 exponentials), alone and beside
+// the MFMA waves: the issue cost of a vector instruction on a SIMD whose
+// other wave streams matrix products, and the product rate beside it.
 // Prints one JSON object.
 #include <hip/hip_runtime.h>
 
@@ -16,9 +22,14 @@
 #include <cstdio>
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 
 constexpr int kLdsIters = 4096;   // 16-byte accesses per lane
 constexpr int kValuIters = 512;   // rounds of 16 instructions per wave
+constexpr int kCoMfma = 1024;     // co-issue: products per chain (4 chains)
+constexpr int kCoValu = 1024;     // co-issue: rounds of 16 vector instructions
 
 template <int WRITE>
 __global__ __launch_bounds__(512) void lds_loop(uint64_t* cycles, uint32_t* sink, int salt) {
@@ -103,6 +114,83 @@ __global__ __launch_bounds__(512) void valu_loop(uint64_t* cycles, float* sink, 
   sink[blockIdx.x * 512 + threadIdx.x] = s;
 }
 
+// PREC 0: bf16 products, 1: fp8; MFMA: whether waves 0..3 run; EXP: 8 of the
+// 16 vector chains are exponentials. Records each wave's own cycles.
+template <int PREC, int MFMA, int EXP>
+__global__ __launch_bounds__(512, 1) void coissue_loop(uint64_t* cycles, float* sink, int seed) {
+  __shared__ float pad[24576];  // 96 KiB: one workgroup per CU
+  const int tid = threadIdx.x, wave = tid / 64;
+  if (tid == 0) pad[seed & 1023] = 1.0f;
+  __syncthreads();
+  float outv = pad[(tid + seed) & 1023];
+  uint64_t t0 = 0, t1 = 0;
+  if (wave < 4) {
+    if (MFMA) {
+      f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+      if (PREC == 0) {
+        bf16x8 a, b;
+        for (int i = 0; i < 8; ++i) {
+          a[i] = (__bf16)(float)((tid + i + seed) & 3);
+          b[i] = (__bf16)(float)((tid * 3 + i) & 3);
+        }
+        t0 = __builtin_amdgcn_s_memtime();
+        for (int it = 0; it < kCoMfma; ++it) {
+          c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+          c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+          c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+        }
+      } else {
+        i32x8 a, b;
+        for (int i = 0; i < 8; ++i) {
+          a[i] = 0x38383838 ^ ((tid + i + seed) & 1);
+          b[i] = 0x30303030;
+        }
+        t0 = __builtin_amdgcn_s_memtime();
+        for (int it = 0; it < kCoMfma; ++it) {
+          c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c0, 0, 0, 0, 127, 0, 127);
+          c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c1, 0, 0, 0, 127, 0, 127);
+          c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c2, 0, 0, 0, 127, 0, 127);
+          c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c3, 0, 0, 0, 127, 0, 127);
+        }
+      }
+      float s = 0.0f;
+      for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+      t1 = __builtin_amdgcn_s_memtime();
+      outv += s;
+    }
+  } else {
+    float x[16];
+    for (int i = 0; i < 16; ++i) x[i] = (float)(seed + i) * 1e-3f;
+    const float h = 0.5f;
+    t0 = __builtin_amdgcn_s_memtime();
+    for (int it = 0; it < kCoValu; ++it) {
+      if (EXP) {
+        asm volatile("v_fma_f32 %0, %0, %8, %8\n\tv_fma_f32 %1, %1, %8, %8\n\t"
+                     "v_fma_f32 %2, %2, %8, %8\n\tv_fma_f32 %3, %3, %8, %8\n\t"
+                     "v_fma_f32 %4, %4, %8, %8\n\tv_fma_f32 %5, %5, %8, %8\n\t"
+                     "v_fma_f32 %6, %6, %8, %8\n\tv_fma_f32 %7, %7, %8, %8"
+                     : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]),
+                       "+v"(x[6]), "+v"(x[7])
+                     : "v"(h));
+        asm volatile("v_exp_f32 %0, %0\n\tv_exp_f32 %1, %1\n\tv_exp_f32 %2, %2\n\t"
+                     "v_exp_f32 %3, %3\n\tv_exp_f32 %4, %4\n\tv_exp_f32 %5, %5\n\t"
+                     "v_exp_f32 %6, %6\n\tv_exp_f32 %7, %7"
+                     : "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]),
+                       "+v"(x[13]), "+v"(x[14]), "+v"(x[15]));
+      } else {
+        RF_FMA16;
+      }
+    }
+    t1 = __builtin_amdgcn_s_memtime();
+    float s = 0.0f;
+    for (int i = 0; i < 16; ++i) s += x[i];
+    outv += s;
+  }
+  if ((tid & 63) == 0) cycles[blockIdx.x * 8 + wave] = t1 - t0;
+  sink[blockIdx.x * 512 + tid] = outv;
+}
+
 int main(int argc, char** argv) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -112,10 +200,10 @@ int main(int argc, char** argv) {
   const int salt = argc > 99 ? 1 : 0;  // 0 at run time, opaque to the compiler
   uint64_t* cyc = nullptr;
   uint32_t* sink = nullptr;
-  if (hipMalloc(&cyc, (size_t)grid * sizeof(uint64_t)) != hipSuccess ||
+  if (hipMalloc(&cyc, (size_t)grid * 8 * sizeof(uint64_t)) != hipSuccess ||
       hipMalloc(&sink, (size_t)grid * 512 * sizeof(uint32_t)) != hipSuccess)
     return 2;
-  uint64_t* h = new uint64_t[grid];
+  uint64_t* h = new uint64_t[grid * 8];
   auto mean_cycles = [&]() -> double {
     if (hipDeviceSynchronize() != hipSuccess ||
         hipMemcpy(h, cyc, (size_t)grid * sizeof(uint64_t), hipMemcpyDeviceToHost) != hipSuccess)
@@ -143,13 +231,46 @@ int main(int argc, char** argv) {
     }
     res[kind] = best;
   }
+  // Co-issue: mean cycles of the MFMA waves and of the vector waves, best of 3.
+  auto co_run = [&](auto kernel, double* mfma, double* valu) -> bool {
+    double bm = 1e300, bv = 1e300;
+    for (int rep = 0; rep < 3; ++rep) {
+      hipLaunchKernelGGL(kernel, dim3(grid), dim3(512), 0, 0, cyc,
+                         reinterpret_cast<float*>(sink), rep);
+      if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+          hipMemcpy(h, cyc, (size_t)grid * 8 * sizeof(uint64_t), hipMemcpyDeviceToHost) !=
+              hipSuccess)
+        return false;
+      double m = 0.0, v = 0.0;
+      for (int i = 0; i < grid; ++i)
+        for (int w = 0; w < 8; ++w) (w < 4 ? m : v) += (double)h[i * 8 + w] / (4.0 * grid);
+      if (m < bm) bm = m;
+      if (v < bv) bv = v;
+    }
+    *mfma = bm / (4.0 * kCoMfma);  // cycles per product
+    *valu = bv / (16.0 * kCoValu); // cycles per vector instruction
+    return true;
+  };
+  double co[6][2];
+  if (!co_run(coissue_loop<0, 0, 0>, &co[0][0], &co[0][1]) ||
+      !co_run(coissue_loop<0, 0, 1>, &co[1][0], &co[1][1]) ||
+      !co_run(coissue_loop<0, 1, 0>, &co[2][0], &co[2][1]) ||
+      !co_run(coissue_loop<0, 1, 1>, &co[3][0], &co[3][1]) ||
+      !co_run(coissue_loop<1, 1, 0>, &co[4][0], &co[4][1]) ||
+      !co_run(coissue_loop<1, 1, 1>, &co[5][0], &co[5][1]))
+    return 2;
   const double lds_bytes = 512.0 * 16 * kLdsIters;      // per workgroup (= per CU)
   const double valu_insts = 2.0 * 16 * kValuIters;      // per SIMD (two waves)
   std::printf("{\"cus\": %d, \"lds_read_B_per_clk_per_cu\": %.1f, "
               "\"lds_write_B_per_clk_per_cu\": %.1f, \"v_exp_f32_cycles\": %.2f, "
-              "\"v_fma_f32_cycles\": %.2f}\n",
+              "\"v_fma_f32_cycles\": %.2f, \"one_wave_fma_cycles\": %.2f, "
+              "\"one_wave_fma_exp_cycles\": %.2f, \"beside_bf16_mfma_fma_cycles\": %.2f, "
+              "\"beside_bf16_mfma_fma_exp_cycles\": %.2f, \"beside_fp8_mfma_fma_cycles\": %.2f, "
+              "\"beside_fp8_mfma_fma_exp_cycles\": %.2f, \"bf16_mfma_cycles_beside_valu\": %.2f, "
+              "\"fp8_mfma_cycles_beside_valu\": %.2f}\n",
               cus, lds_bytes / res[0], lds_bytes / res[1], res[2] / valu_insts,
-              res[3] / valu_insts);
+              res[3] / valu_insts, co[0][1], co[1][1], co[2][1], co[3][1], co[4][1], co[5][1],
+              co[3][0], co[5][0]);
   delete[] h;
   hipFree(cyc);
   hipFree(sink);
